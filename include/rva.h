@@ -1,0 +1,189 @@
+/*
+ * rva.h -- C ABI of the ragged ViT attention library (librva.so), gfx950 only.
+ *
+ * The library implements the pack -> ragged bidirectional attention -> unpack
+ * path for token-pruned Vision Transformers described in "Dispatch-Aware
+ * Ragged Attention for Pruned Vision Transformers" (Abdellatif and Almasri,
+ * arXiv 2604.15408).  The sota2.com page's Abstract frames the pipeline:
+ * after pruning, each image keeps a different number of tokens; those tokens
+ * are packed back to back, attention runs over each image's tokens only, and
+ * the result returns to the padded layout.  The aissential.tech summary's
+ * "Method" section splits the packer into a small index-building phase and a
+ * gather phase.  The same Abstract identifies per-call host dispatch as the
+ * dominant cost at these short lengths, which is why this ABI also offers a
+ * single fused launch and captured launch plans.
+ *
+ * Conventions shared by every entry point
+ * ----------------------------------------
+ *  - All tensor pointers are DEVICE pointers on the current HIP device,
+ *    owned by the caller; the library never allocates or frees them.
+ *    Data pointers must be 16-byte aligned, int32 pointers 4-byte aligned.
+ *  - Padded layout: [B, N, H, d] row-major (token-major, heads inside a
+ *    token row).  Packed layout: [T, H, d] with T = sum of kept counts.
+ *    d (head_dim) must be 64.
+ *  - mask: uint8 [B, N], nonzero = token kept.  Any image may keep 0..N
+ *    tokens.  Kept tokens are packed in ascending token order.
+ *  - cu_seqlens: int32 [B+1], cu[0] = 0, cu[b+1] = cu[b] + n_b (the
+ *    offsets convention of variable-length attention APIs such as the
+ *    FlashAttention-2 varlen interface the Abstract compares against).
+ *  - kept_index: int32 [T], entry cu[b] + r holds b*N + j for the r-th kept
+ *    token j of image b.
+ *  - dtype: RVA_F32 (IEEE binary32), RVA_F16 (binary16) or RVA_BF16
+ *    (bfloat16).  Outputs have the input dtype.  Attention accumulates and
+ *    normalises in fp32; 16-bit inputs use 16-bit matrix-core products with
+ *    fp32 accumulation, fp32 inputs use fp32 matrix-core products.
+ *  - stream: a hipStream_t passed as void* (NULL = the null stream).  Every
+ *    call only enqueues work: no host synchronisation, no device-to-host
+ *    copy, no allocation; results are valid once the stream reaches them.
+ *  - softmax_scale <= 0 (or NaN) selects 1/sqrt(d).
+ *  - Errors: every function returns an rva_status.  All argument checks run
+ *    before anything is enqueued, so a call that fails validation launches
+ *    nothing.  RVA_ERR_HIP reports a HIP runtime failure; rva_last_error()
+ *    then holds the runtime's message (thread-local).
+ *  - Limits: 1 <= B, 1 <= N <= RVA_MAX_TOKENS, 1 <= H <= RVA_MAX_HEADS,
+ *    B * N < 2^31.
+ */
+#ifndef RVA_H
+#define RVA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RVA_MAX_TOKENS 1024
+#define RVA_MAX_HEADS 64
+#define RVA_HEAD_DIM 64
+
+typedef enum { RVA_F32 = 0, RVA_F16 = 1, RVA_BF16 = 2 } rva_dtype;
+
+typedef enum {
+  RVA_OK = 0,
+  RVA_ERR_INVALID = -1,     /* a pointer, size, alignment or dtype is invalid */
+  RVA_ERR_UNSUPPORTED = -2, /* valid request outside what is built (d != 64)   */
+  RVA_ERR_HIP = -3          /* the HIP runtime reported an error               */
+} rva_status;
+
+/*
+ * rva_pack -- kept counts, offsets and the packed gather (both packer phases
+ * of the aissential.tech summary's "Method").
+ *
+ * Computes n_b, cu_seqlens and max_seqlen from mask, then copies the kept
+ * token rows of each non-NULL padded input into its packed output (bit copy).
+ *   q_pad/k_pad/v_pad : [B,N,H,d] inputs; any may be NULL, and then the
+ *                       matching *_out must be NULL too (and is skipped).
+ *   q_out/k_out/v_out : [T,H,d] outputs; capacity of at least T rows (B*N
+ *                       rows always suffices).
+ *   cu_seqlens        : int32[B+1] output (required).
+ *   max_seqlen        : int32[1] output, may be NULL.
+ *   kept_index        : int32[T] output, may be NULL.
+ * Two kernel launches: a one-workgroup count/prefix-sum, then the gather.
+ */
+int rva_pack(const void* q_pad, const void* k_pad, const void* v_pad, const uint8_t* mask,
+             int B, int N, int H, int d, int dtype,
+             void* q_out, void* k_out, void* v_out,
+             int32_t* cu_seqlens, int32_t* max_seqlen, int32_t* kept_index, void* stream);
+
+/*
+ * rva_ragged_attend -- bidirectional attention over each packed sequence
+ * (the sota2.com Abstract's ragged attention kernel; non-causal).
+ *
+ * For every image b and head h: O = softmax(Q K^T * scale) V over rows
+ * cu[b]..cu[b+1]-1 of q/k/v ([T,H,d]), written to o ([T,H,d], capacity T).
+ *   max_seqlen : host-side upper bound on every n_b.  It only sizes the
+ *                on-chip staging; any value >= 1 gives correct results
+ *                (longer sequences are streamed in chunks), the true maximum
+ *                gives the best speed.  <= 0 selects the largest chunk.
+ * One kernel launch of B*H workgroups.
+ */
+int rva_ragged_attend(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                      int B, int H, int d, int max_seqlen, float softmax_scale, int dtype,
+                      void* o, void* stream);
+
+/*
+ * rva_unpack -- packed rows back to the padded layout (the Abstract's
+ * "unpack").  o_pad[b, j] = o_packed[cu[b] + r] for the r-th kept token j of
+ * image b; pruned positions are written as +0.  Every padded row is written
+ * exactly once.  One kernel launch.
+ */
+int rva_unpack(const void* o_packed, const int32_t* cu_seqlens, const uint8_t* mask,
+               int B, int N, int H, int d, int dtype, void* o_pad, void* stream);
+
+/*
+ * rva_fused -- the whole pack -> attend -> unpack path in ONE kernel launch
+ * (the Abstract's dispatch-floor argument taken to its end: padded in,
+ * padded out, no packed intermediate in memory).
+ *   o_pad      : [B,N,H,d] output; pruned positions are +0.
+ *   cu_seqlens : int32[B+1] output or NULL; max_seqlen: int32[1] or NULL.
+ *                When either is given, one extra workgroup of the same launch
+ *                computes them.
+ *   max_seqlen_hint : as rva_ragged_attend's max_seqlen (<= 0 means N).
+ * Results are identical to rva_pack + rva_ragged_attend + rva_unpack.
+ */
+int rva_fused(const void* q_pad, const void* k_pad, const void* v_pad, const uint8_t* mask,
+              int B, int N, int H, int d, int max_seqlen_hint, float softmax_scale, int dtype,
+              void* o_pad, int32_t* cu_seqlens, int32_t* max_seqlen, void* stream);
+
+/*
+ * Launch plans -- capture once, replay with one graph launch per call (the
+ * Abstract's per-call dispatch floor is what this removes).
+ *
+ * mode RVA_PLAN_STAGED : rva_pack, rva_ragged_attend, rva_unpack (4 kernels).
+ *      RVA_PLAN_FUSED  : rva_fused (1 kernel).
+ *      RVA_PLAN_EMPTY  : one empty one-workgroup kernel (measures the floor).
+ * Every pointer and size is fixed at creation; the CONTENTS of the inputs
+ * (including the mask) may change between launches.  Staged mode needs the
+ * packed scratch buffers q/k/v/o_packed (capacity B*N rows each) and
+ * cu_seqlens; kept_index and max_seqlen may be NULL.  Fused mode ignores the
+ * packed buffers; cu_seqlens and max_seqlen may be NULL.
+ * rva_plan_create validates like the direct calls, captures on a private
+ * stream and instantiates a HIP graph (host-side allocation by the runtime);
+ * rva_plan_launch enqueues one graph launch on `stream`.
+ */
+typedef enum { RVA_PLAN_STAGED = 0, RVA_PLAN_FUSED = 1, RVA_PLAN_EMPTY = 2 } rva_plan_mode;
+
+typedef struct {
+  int mode;
+  int B, N, H, d, dtype;
+  int max_seqlen_hint;
+  float softmax_scale;
+  const void* q_pad;
+  const void* k_pad;
+  const void* v_pad;
+  const uint8_t* mask;
+  void* q_packed;
+  void* k_packed;
+  void* v_packed;
+  void* o_packed;
+  int32_t* cu_seqlens;
+  int32_t* max_seqlen;
+  int32_t* kept_index;
+  void* o_pad;
+} rva_plan_desc;
+
+typedef struct rva_plan_s* rva_plan;
+
+int rva_plan_create(const rva_plan_desc* desc, rva_plan* out);
+int rva_plan_launch(rva_plan plan, void* stream);
+int rva_plan_destroy(rva_plan plan);
+
+/*
+ * rva_empty -- enqueue `count` launches of an empty one-workgroup kernel on
+ * `stream` through the same launch path as the entry points above; used to
+ * measure the per-launch dispatch floor the Abstract discusses.
+ */
+int rva_empty(int count, void* stream);
+
+/* Static description of a status code; never NULL. */
+const char* rva_status_string(int status);
+/* Thread-local detail of the last failure on this thread ("" if none). */
+const char* rva_last_error(void);
+/* Library ABI version (major * 10000 + minor * 100 + patch). */
+int rva_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RVA_H */

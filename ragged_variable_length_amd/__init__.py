@@ -1,0 +1,252 @@
+"""Python binding of librva.so (the C ABI in include/rva.h).
+
+Argument marshalling only: tensors are passed as raw device pointers and the
+current torch stream as a hipStream_t.  Every step of pack -> attend ->
+unpack runs in the HIP kernels of librva.so; there is no fallback, and
+importing the binding when the library has not been built raises.
+
+PyTorch supplies device memory and streams; the helpers that allocate
+outputs do so with torch before calling the library.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["RVAError", "lib", "pack", "ragged_attend", "unpack", "fused", "Plan", "empty",
+           "dtype_code", "F32", "F16", "BF16", "STAGED", "FUSED", "EMPTY", "MAX_TOKENS"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "librva.so")
+
+F32, F16, BF16 = 0, 1, 2
+STAGED, FUSED, EMPTY = 0, 1, 2
+MAX_TOKENS = 1024
+HEAD_DIM = 64
+
+_DTYPES = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
+
+
+class RVAError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__(f"{where}: status {status} ({_status_string(status)}): {detail}")
+        self.status = status
+
+
+class _PlanDesc(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int), ("B", ctypes.c_int), ("N", ctypes.c_int),
+                ("H", ctypes.c_int), ("d", ctypes.c_int), ("dtype", ctypes.c_int),
+                ("max_seqlen_hint", ctypes.c_int), ("softmax_scale", ctypes.c_float),
+                ("q_pad", ctypes.c_void_p), ("k_pad", ctypes.c_void_p), ("v_pad", ctypes.c_void_p),
+                ("mask", ctypes.c_void_p), ("q_packed", ctypes.c_void_p),
+                ("k_packed", ctypes.c_void_p), ("v_packed", ctypes.c_void_p),
+                ("o_packed", ctypes.c_void_p), ("cu_seqlens", ctypes.c_void_p),
+                ("max_seqlen", ctypes.c_void_p), ("kept_index", ctypes.c_void_p),
+                ("o_pad", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load librva.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it first (python -c "
+                          "'import __graft_entry__; __graft_entry__.build()')")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    L.rva_pack.argtypes = [P, P, P, P, I, I, I, I, I, P, P, P, P, P, P, P]
+    L.rva_ragged_attend.argtypes = [P, P, P, P, I, I, I, I, F, I, P, P]
+    L.rva_unpack.argtypes = [P, P, P, I, I, I, I, I, P, P]
+    L.rva_fused.argtypes = [P, P, P, P, I, I, I, I, I, F, I, P, P, P, P]
+    L.rva_plan_create.argtypes = [ctypes.POINTER(_PlanDesc), ctypes.POINTER(ctypes.c_void_p)]
+    L.rva_plan_launch.argtypes = [P, P]
+    L.rva_plan_destroy.argtypes = [P]
+    L.rva_empty.argtypes = [I, P]
+    L.rva_status_string.argtypes = [I]
+    L.rva_status_string.restype = ctypes.c_char_p
+    L.rva_last_error.argtypes = []
+    L.rva_last_error.restype = ctypes.c_char_p
+    L.rva_version.argtypes = []
+    for name in ("rva_pack", "rva_ragged_attend", "rva_unpack", "rva_fused", "rva_plan_create",
+                 "rva_plan_launch", "rva_plan_destroy", "rva_empty", "rva_version"):
+        getattr(L, name).restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def _status_string(s: int) -> str:
+    try:
+        return lib().rva_status_string(s).decode()
+    except Exception:  # pragma: no cover - only while reporting another error
+        return "?"
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise RVAError(status, where, lib().rva_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def dtype_code(t: torch.Tensor) -> int:
+    if t.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return _DTYPES[t.dtype]
+
+
+def _mask_u8(mask: torch.Tensor) -> torch.Tensor:
+    if mask.dtype == torch.bool:
+        return mask.view(torch.uint8)
+    if mask.dtype != torch.uint8:
+        raise TypeError("mask must be uint8 or bool")
+    return mask
+
+
+def _req(t: torch.Tensor, name: str):
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous device tensor")
+
+
+def pack(q, k, v, mask, *, outputs=None, kept_index=True, stream=None):
+    """Kept counts, cu_seqlens, max_seqlen and packed q/k/v (capacity B*N rows).
+
+    q/k/v: [B,N,H,64] device tensors (any may be None); mask: [B,N] uint8/bool.
+    Returns dict with q, k, v (packed, [B*N,H,64] capacity), cu_seqlens,
+    max_seqlen ([1] int32) and kept_index ([B*N] capacity int32 or None).
+    """
+    ref = next(t for t in (q, k, v) if t is not None) if any(t is not None for t in (q, k, v)) else None
+    if ref is None:
+        raise ValueError("at least one of q, k, v is needed")
+    B, N, H, d = ref.shape
+    m = _mask_u8(mask)
+    out = dict(outputs or {})
+    dev = ref.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t is not None:
+            _req(t, name)
+            if name not in out:
+                out[name] = torch.empty((B * N, H, d), dtype=t.dtype, device=dev)
+        else:
+            out[name] = None
+    if "cu_seqlens" not in out:
+        out["cu_seqlens"] = torch.empty(B + 1, dtype=torch.int32, device=dev)
+    if "max_seqlen" not in out:
+        out["max_seqlen"] = torch.empty(1, dtype=torch.int32, device=dev)
+    if kept_index and "kept_index" not in out:
+        out["kept_index"] = torch.empty(B * N, dtype=torch.int32, device=dev)
+    out.setdefault("kept_index", None)
+    _check(lib().rva_pack(_ptr(q), _ptr(k), _ptr(v), _ptr(m), B, N, H, d, dtype_code(ref),
+                          _ptr(out["q"]), _ptr(out["k"]), _ptr(out["v"]), _ptr(out["cu_seqlens"]),
+                          _ptr(out["max_seqlen"]), _ptr(out["kept_index"]), _stream(stream)),
+           "rva_pack")
+    return out
+
+
+def ragged_attend(q, k, v, cu_seqlens, max_seqlen: int, *, scale: float | None = None, out=None,
+                  stream=None):
+    """Attention over packed [T,H,64] q/k/v with offsets cu_seqlens [B+1]."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _req(t, name)
+    H, d = q.shape[1], q.shape[2]
+    B = cu_seqlens.shape[0] - 1
+    if out is None:
+        out = torch.empty_like(q)
+    _check(lib().rva_ragged_attend(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), B, H, d,
+                                   int(max_seqlen), float(scale or 0.0), dtype_code(q), _ptr(out),
+                                   _stream(stream)), "rva_ragged_attend")
+    return out
+
+
+def unpack(o_packed, cu_seqlens, mask, *, out=None, stream=None):
+    """Packed [T,H,64] rows -> padded [B,N,H,64]; pruned rows are +0."""
+    m = _mask_u8(mask)
+    B, N = m.shape
+    H, d = o_packed.shape[1], o_packed.shape[2]
+    if out is None:
+        out = torch.empty((B, N, H, d), dtype=o_packed.dtype, device=o_packed.device)
+    _check(lib().rva_unpack(_ptr(o_packed), _ptr(cu_seqlens), _ptr(m), B, N, H, d,
+                            dtype_code(o_packed), _ptr(out), _stream(stream)), "rva_unpack")
+    return out
+
+
+def fused(q, k, v, mask, *, max_seqlen_hint: int = 0, scale: float | None = None, out=None,
+          cu_seqlens=None, max_seqlen=None, stream=None):
+    """Whole path in one launch: padded [B,N,H,64] in, padded out."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _req(t, name)
+    m = _mask_u8(mask)
+    B, N, H, d = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    _check(lib().rva_fused(_ptr(q), _ptr(k), _ptr(v), _ptr(m), B, N, H, d, int(max_seqlen_hint),
+                           float(scale or 0.0), dtype_code(q), _ptr(out), _ptr(cu_seqlens),
+                           _ptr(max_seqlen), _stream(stream)), "rva_fused")
+    return out
+
+
+def empty(count: int = 1, stream=None):
+    """Enqueue `count` empty one-workgroup kernels (dispatch-floor probe)."""
+    _check(lib().rva_empty(int(count), _stream(stream)), "rva_empty")
+
+
+class Plan:
+    """A captured launch sequence (HIP graph) replayed with one launch.
+
+    Tensors given here are kept alive by the plan; their contents may change
+    between launches, their addresses may not.
+    """
+
+    def __init__(self, mode: int, *, q=None, k=None, v=None, mask=None, out=None, scale=None,
+                 max_seqlen_hint: int = 0, packed=None, cu_seqlens=None, max_seqlen=None,
+                 kept_index=None):
+        self._keep = [q, k, v, mask, out, packed, cu_seqlens, max_seqlen, kept_index]
+        desc = _PlanDesc()
+        desc.mode = mode
+        desc.d = HEAD_DIM
+        if mode != EMPTY:
+            B, N, H, d = q.shape
+            desc.B, desc.N, desc.H, desc.d = B, N, H, d
+            desc.dtype = dtype_code(q)
+            desc.max_seqlen_hint = int(max_seqlen_hint)
+            desc.softmax_scale = float(scale or 0.0)
+            desc.q_pad, desc.k_pad, desc.v_pad = q.data_ptr(), k.data_ptr(), v.data_ptr()
+            desc.mask = _mask_u8(mask).data_ptr()
+            desc.o_pad = out.data_ptr()
+            if packed is not None:
+                desc.q_packed = packed["q"].data_ptr()
+                desc.k_packed = packed["k"].data_ptr()
+                desc.v_packed = packed["v"].data_ptr()
+                desc.o_packed = packed["o"].data_ptr()
+            desc.cu_seqlens = cu_seqlens.data_ptr() if cu_seqlens is not None else None
+            desc.max_seqlen = max_seqlen.data_ptr() if max_seqlen is not None else None
+            desc.kept_index = kept_index.data_ptr() if kept_index is not None else None
+        h = ctypes.c_void_p()
+        _check(lib().rva_plan_create(ctypes.byref(desc), ctypes.byref(h)), "rva_plan_create")
+        self._h = h
+
+    def launch(self, stream=None):
+        _check(lib().rva_plan_launch(self._h, _stream(stream)), "rva_plan_launch")
+
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            lib().rva_plan_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

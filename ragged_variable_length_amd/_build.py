@@ -1,0 +1,35 @@
+"""Builds librva.so (gfx950 only) in-tree with hipcc."""
+import os
+import subprocess
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+SOURCES = ["csrc/pack.hip", "csrc/attend.hip", "csrc/rva_host.hip"]
+LIB = os.path.join(PKG, "librva.so")
+
+
+def hipcc_command(out=LIB):
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    return [hipcc, "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+            # no packed fp32 arithmetic anywhere in device code
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-Wall", "-Wno-unused-command-line-argument",
+            "-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc")] + \
+        [os.path.join(PKG, s) for s in SOURCES] + ["-o", out]
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source into librva.so next to this file; returns its path."""
+    tmp = LIB + ".tmp"
+    cmd = hipcc_command(tmp)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + r.stdout + r.stderr)
+    if verbose:
+        print(r.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,518 @@
+// Ragged bidirectional attention, packed and fused forms.
+//
+// What is computed follows "Dispatch-Aware Ragged Attention for Pruned Vision
+// Transformers" (sota2.com page, Abstract): non-causal attention over each
+// image's kept tokens only, O = softmax(Q K^T * scale) V per image and head.
+//
+// Work decomposition (CDNA4 / gfx950):
+//  * one workgroup of 8 waves per (image, head); post-pruning ViT sequences
+//    are short (at most 197 tokens at 224x224, 577 at 384x384), so one
+//    workgroup stages the whole K and V of its sequence on chip once and
+//    every wave reuses them; longer sequences are streamed in chunks;
+//  * each wave owns query blocks of 16 rows (two at a time) and walks the
+//    staged keys 32 at a time with an online softmax in fp32;
+//  * 16-bit inputs: scores are formed transposed, S^T = K Q^T, with the
+//    16x16x32 matrix-core product, so each lane ends up holding one query
+//    column and 4+4 keys -- exactly the per-lane slice the second product
+//    O^T = V^T P^T needs as its B operand.  P never leaves registers; V is
+//    staged transposed (V^T) so its A operand is two 8-byte LDS reads;
+//  * fp32 inputs use the 16x16x4 fp32 matrix-core product with the same
+//    transposed-score layout (no precision is given up for fp32 data);
+//  * row max is shared across the four lanes of a query with two xor
+//    shuffles; row sums stay per lane until the end;
+//  * the fused form first compacts the image's keep-mask row in LDS, reads
+//    Q/K/V rows straight from the padded tensors through that list, writes
+//    O rows straight to padded positions and zero-fills pruned rows.  An
+//    optional extra workgroup computes cu_seqlens / max_seqlen in the same
+//    launch.
+#include <math.h>
+
+#include "rva_device.h"
+#include "rva_internal.h"
+
+namespace rva {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <int DT>
+struct Half16;
+
+template <>
+struct Half16<1> {
+  typedef _Float16 T;
+  typedef f16x8 V8;
+  typedef f16x4 V4;
+  static __device__ __forceinline__ f32x4 mfma(V8 a, V8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <>
+struct Half16<2> {
+  typedef __bf16 T;
+  typedef bf16x8 V8;
+  typedef bf16x4 V4;
+  static __device__ __forceinline__ f32x4 mfma(V8 a, V8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float max8(f32x4 a, f32x4 b) {
+  return fmaxf(fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3])), fmaxf(fmaxf(b[0], b[1]), fmaxf(b[2], b[3])));
+}
+
+// Online-softmax update for one 16-query block and one 32-key tile whose
+// scores are s0 (keys 4g..4g+3) and s1 (keys 16+4g..16+4g+3) in this lane.
+// Returns the probabilities in pr[8] and rescales the running state.
+__device__ __forceinline__ float softmax_step(f32x4& s0, f32x4& s1, int kvalid, float c, float& m,
+                                              float& l, float (&pr)[8]) {
+  const int g = lane_id() >> 4;
+  if (kvalid < kKeyTile) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (4 * g + j >= kvalid) s0[j] = -INFINITY;
+      if (16 + 4 * g + j >= kvalid) s1[j] = -INFINITY;
+    }
+  }
+  float mx = max8(s0, s1);
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float mnew = fmaxf(m, mx * c);
+  const float alpha = fast_exp2(m - mnew);
+  float sum = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    pr[j] = fast_exp2(fmaf(s0[j], c, -mnew));
+    pr[4 + j] = fast_exp2(fmaf(s1[j], c, -mnew));
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) sum += pr[j];
+  l = l * alpha + sum;
+  m = mnew;
+  return alpha;
+}
+
+// ---------------------------------------------------------------- 16-bit
+
+template <int DT>
+__device__ __forceinline__ void tile16(const typename Half16<DT>::T* __restrict__ Ks,
+                                       const typename Half16<DT>::T* __restrict__ Vt, int VP, int k0,
+                                       int kvalid, const typename Half16<DT>::V8 (&qf)[2][2],
+                                       f32x4 (&o)[2][4], float (&m)[2], float (&l)[2], bool two,
+                                       float c) {
+  typedef Half16<DT> Tr;
+  typedef typename Tr::T T;
+  typedef typename Tr::V8 V8;
+  typedef typename Tr::V4 V4;
+  const int lane = lane_id(), g = lane >> 4, r16 = lane & 15;
+  V8 kf[2][2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      kf[kb][ks] = *reinterpret_cast<const V8*>(Ks + (k0 + kb * 16 + r16) * kKPitch16 + ks * 32 + g * 8);
+  V8 vf[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    const T* row = Vt + (db * 16 + r16) * VP + k0 + 4 * g;
+    const V4 lo = *reinterpret_cast<const V4*>(row);
+    const V4 hi = *reinterpret_cast<const V4*>(row + 16);
+    vf[db] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    if (i == 1 && !two) break;
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    s0 = Tr::mfma(kf[0][0], qf[i][0], s0);
+    s1 = Tr::mfma(kf[1][0], qf[i][0], s1);
+    s0 = Tr::mfma(kf[0][1], qf[i][1], s0);
+    s1 = Tr::mfma(kf[1][1], qf[i][1], s1);
+    float pr[8];
+    const float alpha = softmax_step(s0, s1, kvalid, c, m[i], l[i], pr);
+    V8 pf;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) pf[j] = (T)pr[j];
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      o[i][db] *= alpha;
+      o[i][db] = Tr::mfma(vf[db], pf, o[i][db]);
+    }
+  }
+}
+
+// Stage keys [c0, c0 + rows) of the sequence: K rows as they are, V
+// transposed.  V columns [rows, round_up(rows, 32)) are zeroed so masked
+// probabilities (exact zeros) never meet stale LDS contents.
+template <int DT, typename Elem>
+__device__ __forceinline__ void stage16(const typename Half16<DT>::T* __restrict__ kg,
+                                        const typename Half16<DT>::T* __restrict__ vg,
+                                        typename Half16<DT>::T* Ks, typename Half16<DT>::T* Vt, int VP,
+                                        int c0, int rows, Elem elem) {
+  typedef typename Half16<DT>::T T;
+  const int tid = threadIdx.x;
+  const int total = round_up(rows, kKeyTile) * 8;  // 16-byte pieces, <= kKcMax16 * 8
+  u32x4 kr[4], vr[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int e = tid + u * kAttnThreads;
+    kr[u] = u32x4{0u, 0u, 0u, 0u};
+    vr[u] = kr[u];
+    const int r = e >> 3, pc = e & 7;
+    if (e < total && r < rows) {
+      const size_t el = elem(c0 + r) + pc * 8;
+      kr[u] = *reinterpret_cast<const u32x4*>(kg + el);
+      vr[u] = *reinterpret_cast<const u32x4*>(vg + el);
+    }
+  }
+  uint16_t* vt16 = reinterpret_cast<uint16_t*>(Vt);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int e = tid + u * kAttnThreads;
+    if (e < total) {
+      const int r = e >> 3, pc = e & 7;
+      *reinterpret_cast<u32x4*>(Ks + r * kKPitch16 + pc * 8) = kr[u];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        vt16[(pc * 8 + i) * VP + r] = (uint16_t)(vr[u][i >> 1] >> (16 * (i & 1)));
+    }
+  }
+}
+
+template <int DT, typename Elem>
+__device__ __forceinline__ void attend_seq16(const AttnParams& p, int n, unsigned char* kvbase,
+                                             Elem elem) {
+  typedef Half16<DT> Tr;
+  typedef typename Tr::T T;
+  typedef typename Tr::V8 V8;
+  typedef typename Tr::V4 V4;
+  const int lane = lane_id(), w = wave_id(), g = lane >> 4, r16 = lane & 15;
+  const int kc = p.kc, VP = kc + kVPad16;
+  T* Ks = reinterpret_cast<T*>(kvbase);
+  T* Vt = Ks + kc * kKPitch16;
+  const T* __restrict__ qg = static_cast<const T*>(p.q);
+  const T* __restrict__ kg = static_cast<const T*>(p.k);
+  const T* __restrict__ vg = static_cast<const T*>(p.v);
+  T* __restrict__ og = static_cast<T*>(p.o);
+  constexpr int kWaves = kAttnThreads / 64;
+  constexpr int kPerPass = kWaves * kQBlocksPerWave;
+  const int nqb = (n + kQBlock - 1) / kQBlock;
+  const int npass = (nqb + kPerPass - 1) / kPerPass;
+  const int nchunk = (n + kc - 1) / kc;
+  const float c = p.scale_log2e;
+
+  for (int pass = 0; pass < npass; ++pass) {
+    int qb[2];
+    bool act[2];
+    V8 qf[2][2];
+    f32x4 o[2][4];
+    float m[2], l[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      qb[i] = pass * kPerPass + w + i * kWaves;
+      act[i] = qb[i] < nqb;
+      m[i] = -INFINITY;
+      l[i] = 0.f;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[i][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int q = qb[i] * kQBlock + r16;
+      qf[i][0] = V8{};
+      qf[i][1] = V8{};
+      if (act[i] && q < n) {
+        const size_t e = elem(q);
+        qf[i][0] = *reinterpret_cast<const V8*>(qg + e + 8 * g);
+        qf[i][1] = *reinterpret_cast<const V8*>(qg + e + 32 + 8 * g);
+      }
+    }
+    for (int ch = 0; ch < nchunk; ++ch) {
+      const int c0 = ch * kc;
+      const int rows = min(kc, n - c0);
+      if (nchunk > 1 || pass == 0) {
+        if (pass > 0 || ch > 0) __syncthreads();
+        stage16<DT>(kg, vg, Ks, Vt, VP, c0, rows, elem);
+        __syncthreads();
+      }
+      if (act[0]) {
+        const int ntile = (rows + kKeyTile - 1) / kKeyTile;
+        for (int t = 0; t < ntile; ++t) {
+          const int k0 = t * kKeyTile;
+          tile16<DT>(Ks, Vt, VP, k0, min(kKeyTile, rows - k0), qf, o, m, l, act[1], c);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      if (!act[i]) continue;
+      float lt = l[i];
+      lt += __shfl_xor(lt, 16);
+      lt += __shfl_xor(lt, 32);
+      const float inv = 1.f / lt;
+      const int q = qb[i] * kQBlock + r16;
+      if (q < n) {
+        const size_t e = elem(q);
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          V4 out;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) out[j] = (T)(o[i][db][j] * inv);
+          *reinterpret_cast<V4*>(og + e + db * 16 + 4 * g) = out;
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- fp32
+
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// fp32 matrix-core form.  The 16x16x4 product takes one k value per lane
+// group; lane group g covers head dims 16g..16g+15 over 16 steps (any
+// consistent split of the contraction is valid), so each lane's Q and K
+// slices are 64 contiguous bytes.  For P V the k index is the key: step
+// (kb, j) uses key 16kb + 4g + j, which is exactly the score this lane holds.
+__device__ __forceinline__ void tile32(const float* __restrict__ Ks, const float* __restrict__ Vs,
+                                       int k0, int kvalid, const f32x4 (&qf)[2][4],
+                                       f32x4 (&o)[2][4], float (&m)[2], float (&l)[2], bool two,
+                                       float c) {
+  const int lane = lane_id(), g = lane >> 4, r16 = lane & 15;
+  f32x4 kf[2][4];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4)
+      kf[kb][t4] = *reinterpret_cast<const f32x4*>(Ks + (k0 + kb * 16 + r16) * kPitch32 + 16 * g + 4 * t4);
+  float va[4][8];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      va[db][j] = Vs[(k0 + (j >> 2) * 16 + 4 * g + (j & 3)) * kPitch32 + db * 16 + r16];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    if (i == 1 && !two) break;
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      s0 = mfma_f32(kf[0][t >> 2][t & 3], qf[i][t >> 2][t & 3], s0);
+      s1 = mfma_f32(kf[1][t >> 2][t & 3], qf[i][t >> 2][t & 3], s1);
+    }
+    float pr[8];
+    const float alpha = softmax_step(s0, s1, kvalid, c, m[i], l[i], pr);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      o[i][db] *= alpha;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) o[i][db] = mfma_f32(va[db][j], pr[j], o[i][db]);
+    }
+  }
+}
+
+template <typename Elem>
+__device__ __forceinline__ void stage32(const float* __restrict__ kg, const float* __restrict__ vg,
+                                        float* Ks, float* Vs, int c0, int rows, Elem elem) {
+  const int tid = threadIdx.x;
+  const int total = round_up(rows, kKeyTile) * 16;  // <= kKcMax32 * 16
+  u32x4 kr[4], vr[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int e = tid + u * kAttnThreads;
+    kr[u] = u32x4{0u, 0u, 0u, 0u};
+    vr[u] = kr[u];
+    const int r = e >> 4, pc = e & 15;
+    if (e < total && r < rows) {
+      const size_t el = elem(c0 + r) + pc * 4;
+      kr[u] = *reinterpret_cast<const u32x4*>(kg + el);
+      vr[u] = *reinterpret_cast<const u32x4*>(vg + el);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int e = tid + u * kAttnThreads;
+    if (e < total) {
+      const int r = e >> 4, pc = e & 15;
+      *reinterpret_cast<u32x4*>(Ks + r * kPitch32 + pc * 4) = kr[u];
+      *reinterpret_cast<u32x4*>(Vs + r * kPitch32 + pc * 4) = vr[u];
+    }
+  }
+}
+
+template <typename Elem>
+__device__ __forceinline__ void attend_seq32(const AttnParams& p, int n, unsigned char* kvbase,
+                                             Elem elem) {
+  const int lane = lane_id(), w = wave_id(), g = lane >> 4, r16 = lane & 15;
+  const int kc = p.kc;
+  float* Ks = reinterpret_cast<float*>(kvbase);
+  float* Vs = Ks + kc * kPitch32;
+  const float* __restrict__ qg = static_cast<const float*>(p.q);
+  const float* __restrict__ kg = static_cast<const float*>(p.k);
+  const float* __restrict__ vg = static_cast<const float*>(p.v);
+  float* __restrict__ og = static_cast<float*>(p.o);
+  constexpr int kWaves = kAttnThreads / 64;
+  constexpr int kPerPass = kWaves * kQBlocksPerWave;
+  const int nqb = (n + kQBlock - 1) / kQBlock;
+  const int npass = (nqb + kPerPass - 1) / kPerPass;
+  const int nchunk = (n + kc - 1) / kc;
+  const float c = p.scale_log2e;
+
+  for (int pass = 0; pass < npass; ++pass) {
+    int qb[2];
+    bool act[2];
+    f32x4 qf[2][4];
+    f32x4 o[2][4];
+    float m[2], l[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      qb[i] = pass * kPerPass + w + i * kWaves;
+      act[i] = qb[i] < nqb;
+      m[i] = -INFINITY;
+      l[i] = 0.f;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[i][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int q = qb[i] * kQBlock + r16;
+#pragma unroll
+      for (int t4 = 0; t4 < 4; ++t4) qf[i][t4] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (act[i] && q < n) {
+        const size_t e = elem(q);
+#pragma unroll
+        for (int t4 = 0; t4 < 4; ++t4) qf[i][t4] = *reinterpret_cast<const f32x4*>(qg + e + 16 * g + 4 * t4);
+      }
+    }
+    for (int ch = 0; ch < nchunk; ++ch) {
+      const int c0 = ch * kc;
+      const int rows = min(kc, n - c0);
+      if (nchunk > 1 || pass == 0) {
+        if (pass > 0 || ch > 0) __syncthreads();
+        stage32(kg, vg, Ks, Vs, c0, rows, elem);
+        __syncthreads();
+      }
+      if (act[0]) {
+        const int ntile = (rows + kKeyTile - 1) / kKeyTile;
+        for (int t = 0; t < ntile; ++t) {
+          const int k0 = t * kKeyTile;
+          tile32(Ks, Vs, k0, min(kKeyTile, rows - k0), qf, o, m, l, act[1], c);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      if (!act[i]) continue;
+      float lt = l[i];
+      lt += __shfl_xor(lt, 16);
+      lt += __shfl_xor(lt, 32);
+      const float inv = 1.f / lt;
+      const int q = qb[i] * kQBlock + r16;
+      if (q < n) {
+        const size_t e = elem(q);
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+          *reinterpret_cast<f32x4*>(og + e + db * 16 + 4 * g) = o[i][db] * inv;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- kernels
+
+// Zero the output rows of pruned tokens of image b, head h (fused form).
+template <int ESIZE>
+__device__ __forceinline__ void zero_pruned(void* o, const uint64_t* ballots, int b, int N, int H,
+                                            int h) {
+  constexpr int PIECES = kHeadDim * ESIZE / 16;
+  const int total = N * PIECES;
+  char* base = static_cast<char*>(o);
+  for (int e = threadIdx.x; e < total; e += kAttnThreads) {
+    const int j = e / PIECES, pc = e - j * PIECES;
+    const bool kept = (ballots[j >> 6] >> (j & 63)) & 1ull;
+    if (!kept)
+      *reinterpret_cast<u32x4*>(base + (((size_t)b * N + j) * H + h) * (kHeadDim * ESIZE) + pc * 16) =
+          u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+template <int DT, bool FUSED>
+__global__ __launch_bounds__(kAttnThreads) void attend_kernel(AttnParams p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  int bid = blockIdx.x;
+  if constexpr (FUSED) {
+    if (p.cu_out || p.max_out) {
+      if (bid == 0) {
+        count_scan_block<kAttnThreads>(p.mask, p.B, p.N, p.cu_out, p.max_out,
+                                       reinterpret_cast<int*>(smem));
+        return;
+      }
+      --bid;
+    }
+  }
+  const int b = bid / p.H, h = bid - b * p.H;
+  const int H = p.H, N = p.N;
+  if constexpr (FUSED) {
+    int32_t* idx = reinterpret_cast<int32_t*>(smem);
+    const size_t off = (size_t)round_up(N * 4, 16);
+    uint64_t* ballots = reinterpret_cast<uint64_t*>(smem + off);
+    int32_t* cnt = reinterpret_cast<int32_t*>(smem + off + 16 * 8);
+    const int n = compact_row<kAttnThreads>(p.mask + (size_t)b * N, N, idx, nullptr, ballots, cnt);
+    zero_pruned<DT == 0 ? 4 : 2>(p.o, ballots, b, N, H, h);
+    if (n <= 0) return;
+    unsigned char* kvbase = smem + attn_compact_bytes(N);
+    auto elem = [=](int r) -> size_t { return (((size_t)b * N + idx[r]) * H + h) * kHeadDim; };
+    if constexpr (DT == 0)
+      attend_seq32(p, n, kvbase, elem);
+    else
+      attend_seq16<DT>(p, n, kvbase, elem);
+  } else {
+    const int row0 = p.cu[b];
+    const int n = p.cu[b + 1] - row0;
+    if (n <= 0) return;
+    auto elem = [=](int r) -> size_t { return (((size_t)row0 + r) * H + h) * kHeadDim; };
+    if constexpr (DT == 0)
+      attend_seq32(p, n, smem, elem);
+    else
+      attend_seq16<DT>(p, n, smem, elem);
+  }
+}
+
+template <int DT, bool FUSED>
+static hipError_t set_lds_limit() {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(&attend_kernel<DT, FUSED>),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+}
+
+hipError_t attend_init() {
+  hipError_t e;
+  if ((e = set_lds_limit<0, false>()) != hipSuccess) return e;
+  if ((e = set_lds_limit<1, false>()) != hipSuccess) return e;
+  if ((e = set_lds_limit<2, false>()) != hipSuccess) return e;
+  if ((e = set_lds_limit<0, true>()) != hipSuccess) return e;
+  if ((e = set_lds_limit<1, true>()) != hipSuccess) return e;
+  return set_lds_limit<2, true>();
+}
+
+template <int DT, bool FUSED>
+static void launch_one(const AttnParams& p, int grid, size_t lds, hipStream_t s) {
+  hipLaunchKernelGGL((attend_kernel<DT, FUSED>), dim3(grid), dim3(kAttnThreads), lds, s, p);
+}
+
+hipError_t launch_attend(const AttnParams& p, int dtype, bool fused, hipStream_t s) {
+  const size_t lds = attn_lds_bytes(dtype, fused, p.N, p.kc);
+  const int grid = p.B * p.H + ((fused && (p.cu_out || p.max_out)) ? 1 : 0);
+  if (fused) {
+    if (dtype == 0) launch_one<0, true>(p, grid, lds, s);
+    else if (dtype == 1) launch_one<1, true>(p, grid, lds, s);
+    else launch_one<2, true>(p, grid, lds, s);
+  } else {
+    if (dtype == 0) launch_one<0, false>(p, grid, lds, s);
+    else if (dtype == 1) launch_one<1, false>(p, grid, lds, s);
+    else launch_one<2, false>(p, grid, lds, s);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace rva

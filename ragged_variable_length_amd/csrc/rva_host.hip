@@ -1,0 +1,391 @@
+// Host side of the C ABI declared in include/rva.h: argument validation,
+// launch geometry, thread-local error text and captured launch plans.
+// Nothing here allocates device memory or synchronises with the device.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <new>
+
+#include "rva.h"
+#include "rva_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(RVA_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t esize(int dtype) { return dtype == RVA_F32 ? 4 : 2; }
+
+int check_shape(int B, int N, int H, int d, int dtype) {
+  if (dtype != RVA_F32 && dtype != RVA_F16 && dtype != RVA_BF16)
+    return fail(RVA_ERR_INVALID, "unknown dtype %d", dtype);
+  if (B < 1) return fail(RVA_ERR_INVALID, "B must be >= 1 (got %d)", B);
+  if (N < 1 || N > RVA_MAX_TOKENS)
+    return fail(RVA_ERR_INVALID, "N must be in [1, %d] (got %d)", RVA_MAX_TOKENS, N);
+  if (H < 1 || H > RVA_MAX_HEADS)
+    return fail(RVA_ERR_INVALID, "H must be in [1, %d] (got %d)", RVA_MAX_HEADS, H);
+  if ((long long)B * N >= (1ll << 31)) return fail(RVA_ERR_INVALID, "B*N must be < 2^31");
+  if (d != RVA_HEAD_DIM) return fail(RVA_ERR_UNSUPPORTED, "head_dim %d unsupported (only 64)", d);
+  return RVA_OK;
+}
+
+int check_data(const void* p, const char* name, bool required) {
+  if (!p) return required ? fail(RVA_ERR_INVALID, "%s is NULL", name) : RVA_OK;
+  if (!aligned(p, 16)) return fail(RVA_ERR_INVALID, "%s is not 16-byte aligned", name);
+  return RVA_OK;
+}
+
+int check_i32(const void* p, const char* name, bool required) {
+  if (!p) return required ? fail(RVA_ERR_INVALID, "%s is NULL", name) : RVA_OK;
+  if (!aligned(p, 4)) return fail(RVA_ERR_INVALID, "%s is not 4-byte aligned", name);
+  return RVA_OK;
+}
+
+#define RVA_TRY(x)            \
+  do {                        \
+    int _s = (x);             \
+    if (_s != RVA_OK) return _s; \
+  } while (0)
+
+std::once_flag g_init_once;
+hipError_t g_init_err = hipSuccess;
+
+int ensure_init() {
+  std::call_once(g_init_once, [] { g_init_err = rva::attend_init(); });
+  if (g_init_err != hipSuccess) return hip_fail(g_init_err, "attention kernel set-up");
+  return RVA_OK;
+}
+
+float resolve_scale(float s, int d) {
+  if (!(s > 0.f)) s = 1.0f / sqrtf((float)d);
+  return s * 1.4426950408889634f;  // fold log2(e) so the kernel uses exp2
+}
+
+int pick_kc(int dtype, int hint, int fallback) {
+  const int cap = rva::attn_kc_max(dtype);
+  int n = hint > 0 ? hint : fallback;
+  if (n < 1) n = cap;
+  int kc = rva::round_up(n, rva::kKeyTile);
+  return kc > cap ? cap : kc;
+}
+
+// Row splits for the copy kernels: aim for enough workgroups to cover the
+// device when the batch is small.
+int copy_splits(int B, int N) {
+  int s = 1;
+  while (s < 8 && B * s < 512 && (N / (s * 2)) >= 16) s *= 2;
+  return s;
+}
+
+// ---- validated argument bundles (validation never launches anything)
+
+struct PackArgs {
+  rva::CopyParams cp;
+  int32_t* max_seqlen;
+  int splits;
+};
+
+int validate_pack(const void* q_pad, const void* k_pad, const void* v_pad, const uint8_t* mask,
+                  int B, int N, int H, int d, int dtype, void* q_out, void* k_out, void* v_out,
+                  int32_t* cu, int32_t* max_seqlen, int32_t* kept_index, PackArgs* out) {
+  RVA_TRY(check_shape(B, N, H, d, dtype));
+  if (!mask) return fail(RVA_ERR_INVALID, "mask is NULL");
+  const void* in[3] = {q_pad, k_pad, v_pad};
+  void* outp[3] = {q_out, k_out, v_out};
+  const char* nin[3] = {"q_pad", "k_pad", "v_pad"};
+  const char* nout[3] = {"q_out", "k_out", "v_out"};
+  for (int t = 0; t < 3; ++t) {
+    if ((in[t] == nullptr) != (outp[t] == nullptr))
+      return fail(RVA_ERR_INVALID, "%s and %s must both be given or both be NULL", nin[t], nout[t]);
+    RVA_TRY(check_data(in[t], nin[t], false));
+    RVA_TRY(check_data(outp[t], nout[t], false));
+  }
+  RVA_TRY(check_i32(cu, "cu_seqlens", true));
+  RVA_TRY(check_i32(max_seqlen, "max_seqlen", false));
+  RVA_TRY(check_i32(kept_index, "kept_index", false));
+  rva::CopyParams& p = out->cp;
+  for (int t = 0; t < 3; ++t) {
+    p.src[t] = in[t];
+    p.dst[t] = outp[t];
+  }
+  p.mask = mask;
+  p.cu = cu;
+  p.kept_index = kept_index;
+  p.B = B;
+  p.N = N;
+  p.row_bytes = (int)(H * d * esize(dtype));
+  out->max_seqlen = max_seqlen;
+  out->splits = copy_splits(B, N);
+  return RVA_OK;
+}
+
+int enqueue_pack(const PackArgs& a, hipStream_t s) {
+  hipError_t e = rva::launch_count_scan(a.cp.mask, a.cp.B, a.cp.N, const_cast<int32_t*>(a.cp.cu),
+                                        a.max_seqlen, s);
+  if (e != hipSuccess) return hip_fail(e, "count/scan launch");
+  bool any = a.cp.src[0] || a.cp.src[1] || a.cp.src[2] || a.cp.kept_index;
+  if (any) {
+    e = rva::launch_pack(a.cp, a.splits, s);
+    if (e != hipSuccess) return hip_fail(e, "pack launch");
+  }
+  return RVA_OK;
+}
+
+int validate_attend(const void* q, const void* k, const void* v, const int32_t* cu, int B, int H,
+                    int d, int max_seqlen, float scale, int dtype, void* o, rva::AttnParams* p) {
+  RVA_TRY(check_shape(B, 1, H, d, dtype));
+  RVA_TRY(check_data(q, "q", true));
+  RVA_TRY(check_data(k, "k", true));
+  RVA_TRY(check_data(v, "v", true));
+  RVA_TRY(check_data(o, "o", true));
+  RVA_TRY(check_i32(cu, "cu_seqlens", true));
+  memset(p, 0, sizeof(*p));
+  p->q = q;
+  p->k = k;
+  p->v = v;
+  p->o = o;
+  p->cu = cu;
+  p->B = B;
+  p->N = 0;
+  p->H = H;
+  p->kc = pick_kc(dtype, max_seqlen, 0);
+  p->scale_log2e = resolve_scale(scale, d);
+  return RVA_OK;
+}
+
+int validate_unpack(const void* o_packed, const int32_t* cu, const uint8_t* mask, int B, int N,
+                    int H, int d, int dtype, void* o_pad, PackArgs* out) {
+  RVA_TRY(check_shape(B, N, H, d, dtype));
+  if (!mask) return fail(RVA_ERR_INVALID, "mask is NULL");
+  RVA_TRY(check_data(o_packed, "o_packed", true));
+  RVA_TRY(check_data(o_pad, "o_pad", true));
+  RVA_TRY(check_i32(cu, "cu_seqlens", true));
+  rva::CopyParams& p = out->cp;
+  memset(&p, 0, sizeof(p));
+  p.src[0] = o_packed;
+  p.dst[0] = o_pad;
+  p.mask = mask;
+  p.cu = cu;
+  p.B = B;
+  p.N = N;
+  p.row_bytes = (int)(H * d * esize(dtype));
+  out->max_seqlen = nullptr;
+  out->splits = copy_splits(B, N);
+  return RVA_OK;
+}
+
+int validate_fused(const void* q, const void* k, const void* v, const uint8_t* mask, int B, int N,
+                   int H, int d, int hint, float scale, int dtype, void* o, int32_t* cu,
+                   int32_t* max_seqlen, rva::AttnParams* p) {
+  RVA_TRY(check_shape(B, N, H, d, dtype));
+  if (!mask) return fail(RVA_ERR_INVALID, "mask is NULL");
+  RVA_TRY(check_data(q, "q_pad", true));
+  RVA_TRY(check_data(k, "k_pad", true));
+  RVA_TRY(check_data(v, "v_pad", true));
+  RVA_TRY(check_data(o, "o_pad", true));
+  RVA_TRY(check_i32(cu, "cu_seqlens", false));
+  RVA_TRY(check_i32(max_seqlen, "max_seqlen", false));
+  memset(p, 0, sizeof(*p));
+  p->q = q;
+  p->k = k;
+  p->v = v;
+  p->o = o;
+  p->mask = mask;
+  p->cu_out = cu;
+  p->max_out = max_seqlen;
+  p->B = B;
+  p->N = N;
+  p->H = H;
+  p->kc = pick_kc(dtype, hint > 0 && hint < N ? hint : N, N);
+  p->scale_log2e = resolve_scale(scale, d);
+  return RVA_OK;
+}
+
+int enqueue_attend(const rva::AttnParams& p, int dtype, bool fused, hipStream_t s) {
+  RVA_TRY(ensure_init());
+  hipError_t e = rva::launch_attend(p, dtype, fused, s);
+  if (e != hipSuccess) return hip_fail(e, fused ? "fused launch" : "attention launch");
+  return RVA_OK;
+}
+
+}  // namespace
+
+struct rva_plan_s {
+  hipGraph_t graph;
+  hipGraphExec_t exec;
+};
+
+extern "C" {
+
+int rva_version(void) { return 100; }
+
+const char* rva_status_string(int status) {
+  switch (status) {
+    case RVA_OK: return "ok";
+    case RVA_ERR_INVALID: return "invalid argument";
+    case RVA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case RVA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* rva_last_error(void) { return g_err; }
+
+int rva_pack(const void* q_pad, const void* k_pad, const void* v_pad, const uint8_t* mask, int B,
+             int N, int H, int d, int dtype, void* q_out, void* k_out, void* v_out,
+             int32_t* cu_seqlens, int32_t* max_seqlen, int32_t* kept_index, void* stream) {
+  PackArgs a;
+  RVA_TRY(validate_pack(q_pad, k_pad, v_pad, mask, B, N, H, d, dtype, q_out, k_out, v_out,
+                        cu_seqlens, max_seqlen, kept_index, &a));
+  return enqueue_pack(a, static_cast<hipStream_t>(stream));
+}
+
+int rva_ragged_attend(const void* q, const void* k, const void* v, const int32_t* cu_seqlens, int B,
+                      int H, int d, int max_seqlen, float softmax_scale, int dtype, void* o,
+                      void* stream) {
+  rva::AttnParams p;
+  RVA_TRY(validate_attend(q, k, v, cu_seqlens, B, H, d, max_seqlen, softmax_scale, dtype, o, &p));
+  return enqueue_attend(p, dtype, false, static_cast<hipStream_t>(stream));
+}
+
+int rva_unpack(const void* o_packed, const int32_t* cu_seqlens, const uint8_t* mask, int B, int N,
+               int H, int d, int dtype, void* o_pad, void* stream) {
+  PackArgs a;
+  RVA_TRY(validate_unpack(o_packed, cu_seqlens, mask, B, N, H, d, dtype, o_pad, &a));
+  hipError_t e = rva::launch_unpack(a.cp, a.splits, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "unpack launch");
+  return RVA_OK;
+}
+
+int rva_fused(const void* q_pad, const void* k_pad, const void* v_pad, const uint8_t* mask, int B,
+              int N, int H, int d, int max_seqlen_hint, float softmax_scale, int dtype, void* o_pad,
+              int32_t* cu_seqlens, int32_t* max_seqlen, void* stream) {
+  rva::AttnParams p;
+  RVA_TRY(validate_fused(q_pad, k_pad, v_pad, mask, B, N, H, d, max_seqlen_hint, softmax_scale,
+                         dtype, o_pad, cu_seqlens, max_seqlen, &p));
+  return enqueue_attend(p, dtype, true, static_cast<hipStream_t>(stream));
+}
+
+int rva_empty(int count, void* stream) {
+  if (count < 0) return fail(RVA_ERR_INVALID, "count must be >= 0");
+  for (int i = 0; i < count; ++i) {
+    hipError_t e = rva::launch_empty(static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "empty launch");
+  }
+  return RVA_OK;
+}
+
+int rva_plan_create(const rva_plan_desc* desc, rva_plan* out) {
+  if (!desc || !out) return fail(RVA_ERR_INVALID, "desc and out must be non-NULL");
+  *out = nullptr;
+  const rva_plan_desc& D = *desc;
+  PackArgs pack, unpack;
+  rva::AttnParams attn;
+  switch (D.mode) {
+    case RVA_PLAN_STAGED:
+      RVA_TRY(validate_pack(D.q_pad, D.k_pad, D.v_pad, D.mask, D.B, D.N, D.H, D.d, D.dtype,
+                            D.q_packed, D.k_packed, D.v_packed, D.cu_seqlens, D.max_seqlen,
+                            D.kept_index, &pack));
+      if (!D.q_pad || !D.k_pad || !D.v_pad)
+        return fail(RVA_ERR_INVALID, "staged plan needs q, k and v");
+      RVA_TRY(validate_attend(D.q_packed, D.k_packed, D.v_packed, D.cu_seqlens, D.B, D.H, D.d,
+                              D.max_seqlen_hint > 0 ? D.max_seqlen_hint : D.N, D.softmax_scale,
+                              D.dtype, D.o_packed, &attn));
+      RVA_TRY(validate_unpack(D.o_packed, D.cu_seqlens, D.mask, D.B, D.N, D.H, D.d, D.dtype,
+                              D.o_pad, &unpack));
+      break;
+    case RVA_PLAN_FUSED:
+      RVA_TRY(validate_fused(D.q_pad, D.k_pad, D.v_pad, D.mask, D.B, D.N, D.H, D.d,
+                             D.max_seqlen_hint, D.softmax_scale, D.dtype, D.o_pad, D.cu_seqlens,
+                             D.max_seqlen, &attn));
+      break;
+    case RVA_PLAN_EMPTY:
+      break;
+    default:
+      return fail(RVA_ERR_INVALID, "unknown plan mode %d", D.mode);
+  }
+  RVA_TRY(ensure_init());
+
+  hipStream_t cs = nullptr;
+  hipError_t e = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking);
+  if (e != hipSuccess) return hip_fail(e, "capture stream");
+  e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+  if (e != hipSuccess) {
+    (void)hipStreamDestroy(cs);
+    return hip_fail(e, "begin capture");
+  }
+  int st = RVA_OK;
+  switch (D.mode) {
+    case RVA_PLAN_STAGED:
+      st = enqueue_pack(pack, cs);
+      if (st == RVA_OK) st = enqueue_attend(attn, D.dtype, false, cs);
+      if (st == RVA_OK) {
+        e = rva::launch_unpack(unpack.cp, unpack.splits, cs);
+        if (e != hipSuccess) st = hip_fail(e, "unpack launch");
+      }
+      break;
+    case RVA_PLAN_FUSED:
+      st = enqueue_attend(attn, D.dtype, true, cs);
+      break;
+    case RVA_PLAN_EMPTY:
+      e = rva::launch_empty(cs);
+      if (e != hipSuccess) st = hip_fail(e, "empty launch");
+      break;
+  }
+  hipGraph_t graph = nullptr;
+  hipError_t ee = hipStreamEndCapture(cs, &graph);
+  (void)hipStreamDestroy(cs);
+  if (st != RVA_OK) {
+    if (graph) (void)hipGraphDestroy(graph);
+    return st;
+  }
+  if (ee != hipSuccess) return hip_fail(ee, "end capture");
+  hipGraphExec_t exec = nullptr;
+  e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+  if (e != hipSuccess) {
+    (void)hipGraphDestroy(graph);
+    return hip_fail(e, "graph instantiate");
+  }
+  rva_plan_s* plan = new (std::nothrow) rva_plan_s{graph, exec};
+  if (!plan) {
+    (void)hipGraphExecDestroy(exec);
+    (void)hipGraphDestroy(graph);
+    return fail(RVA_ERR_INVALID, "out of host memory");
+  }
+  *out = plan;
+  return RVA_OK;
+}
+
+int rva_plan_launch(rva_plan plan, void* stream) {
+  if (!plan) return fail(RVA_ERR_INVALID, "plan is NULL");
+  hipError_t e = hipGraphLaunch(plan->exec, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "graph launch");
+  return RVA_OK;
+}
+
+int rva_plan_destroy(rva_plan plan) {
+  if (!plan) return RVA_OK;
+  (void)hipGraphExecDestroy(plan->exec);
+  (void)hipGraphDestroy(plan->graph);
+  delete plan;
+  return RVA_OK;
+}
+
+}  // extern "C"

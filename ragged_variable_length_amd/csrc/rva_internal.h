@@ -1,0 +1,79 @@
+// Internal interface between the host API (rva_host.hip) and the kernel
+// translation units.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace rva {
+
+constexpr int kHeadDim = 64;
+constexpr int kAttnThreads = 512;   // 8 waves of 64 lanes per attention workgroup
+constexpr int kQBlock = 16;         // query rows per matrix-core block
+constexpr int kQBlocksPerWave = 2;  // query blocks a wave carries through one pass
+constexpr int kKeyTile = 32;        // keys per inner step
+constexpr int kPackThreads = 256;
+constexpr int kScanThreads = 1024;
+
+// Keys staged on chip per chunk.  16-bit: K rows [kc][72] + V^T [64][kc + 8]
+// halves; fp32: K and V rows [kc][68] floats.
+constexpr int kKcMax16 = 256;
+constexpr int kKcMax32 = 128;
+constexpr int kKPitch16 = 72;  // halves per staged K row (64 + 8 pad: keeps 16 B alignment)
+constexpr int kVPad16 = 8;     // halves of pad per staged V^T row
+constexpr int kPitch32 = 68;   // floats per staged K/V row for fp32
+
+struct AttnParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  const int32_t* cu;      // packed mode: offsets int32[B+1]
+  const uint8_t* mask;    // fused mode: uint8[B,N]
+  int32_t* cu_out;        // fused mode: optional offsets output
+  int32_t* max_out;       // fused mode: optional max kept count output
+  int B, N, H;
+  int kc;                 // keys per staged chunk (multiple of kKeyTile)
+  float scale_log2e;      // softmax scale * log2(e)
+};
+
+struct CopyParams {
+  const void* src[3];     // pack: padded q/k/v (NULL = skip); unpack: src[0] = packed o
+  void* dst[3];           // pack: packed q/k/v; unpack: dst[0] = padded o
+  const uint8_t* mask;
+  const int32_t* cu;
+  int32_t* kept_index;    // pack only, optional
+  int B, N;
+  int row_bytes;          // H * d * element size (multiple of 16)
+};
+
+__host__ __device__ inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
+
+inline int attn_kc_max(int dtype) { return dtype == 0 ? kKcMax32 : kKcMax16; }
+
+// Bytes of the compaction area at the start of the fused kernel's LDS:
+// kept list int32[N], 16 per-chunk ballots (u64), 16 chunk counts (int32).
+__host__ __device__ inline size_t attn_compact_bytes(int N) {
+  return (size_t)round_up(N * 4, 16) + 16 * 8 + 16 * 4;
+}
+
+inline size_t attn_lds_bytes(int dtype, bool fused, int N, int kc) {
+  size_t kv = dtype == 0 ? (size_t)kc * kPitch32 * 4 * 2
+                         : (size_t)kc * kKPitch16 * 2 + (size_t)kHeadDim * (kc + kVPad16) * 2;
+  size_t head = fused ? attn_compact_bytes(N) : 0;
+  size_t scan = (size_t)(kAttnThreads + 64) * 4;  // fused scan workgroup reuses LDS
+  size_t total = head + kv;
+  return total > scan ? total : scan;
+}
+
+// Launchers (enqueue only; return the launch status).
+hipError_t launch_count_scan(const uint8_t* mask, int B, int N, int32_t* cu, int32_t* max_out,
+                             hipStream_t s);
+hipError_t launch_pack(const CopyParams& p, int splits, hipStream_t s);
+hipError_t launch_unpack(const CopyParams& p, int splits, hipStream_t s);
+hipError_t launch_attend(const AttnParams& p, int dtype, bool fused, hipStream_t s);
+hipError_t launch_empty(hipStream_t s);
+hipError_t attend_init();  // raises the dynamic-LDS limit of every attention kernel
+
+}  // namespace rva

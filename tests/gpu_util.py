@@ -1,0 +1,48 @@
+"""Helpers for the GPU tests: moving workloads to the device and comparing
+device results with the oracle.  Imports torch lazily-safe (CPU-only hosts
+can import this module)."""
+import numpy as np
+import torch
+
+TOL = {"f16": 2e-3, "bf16": 1e-2, "f32": 1e-4}
+
+
+def to_dev(x: np.ndarray, dtype: str, dev) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    if dtype == "bf16":
+        t = t.view(torch.int16).to(dev).view(torch.bfloat16)
+    else:
+        t = t.to(dev)
+    return t
+
+
+def upload(w, dev):
+    q, k, v = (to_dev(x, w.dtype, dev) for x in (w.q, w.k, w.v))
+    mask = torch.from_numpy(w.mask).to(dev)
+    return q, k, v, mask
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    """Raw bits of a device tensor as a numpy unsigned array."""
+    t = t.detach().contiguous().cpu()
+    if t.element_size() == 2:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    if t.element_size() == 4:
+        return t.view(torch.int32).numpy().view(np.uint32)
+    return t.numpy()
+
+
+def host_bits(x: np.ndarray) -> np.ndarray:
+    x = np.ascontiguousarray(x)
+    return x.view(np.uint16) if x.itemsize == 2 else x.view(np.uint32)
+
+
+def f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def max_err(got: np.ndarray, ref: np.ndarray) -> float:
+    if got.size == 0:
+        return 0.0
+    assert np.isfinite(got).all(), "non-finite value in device output"
+    return float(np.abs(got - ref).max())

@@ -1,0 +1,108 @@
+"""Host-only checks of the C ABI: the library loads, exports every function
+include/rva.h declares, and rejects invalid arguments before touching the
+device (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rva.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(rva_[a-z_]+)\s*\(",
+                       src, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def L():
+    import ragged_variable_length_amd as rva
+    if not os.path.exists(rva.LIB_PATH):
+        from ragged_variable_length_amd import _build
+        _build.build()
+    return rva.lib()
+
+
+def test_header_lists_the_entry_points():
+    names = _declared()
+    for want in ("rva_pack", "rva_ragged_attend", "rva_unpack", "rva_fused", "rva_plan_create",
+                 "rva_plan_launch", "rva_plan_destroy", "rva_empty", "rva_status_string",
+                 "rva_last_error", "rva_version"):
+        assert want in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    for name in _declared():
+        assert hasattr(L, name), name
+
+
+def test_status_strings(L):
+    assert L.rva_status_string(0) == b"ok"
+    assert L.rva_status_string(-1) == b"invalid argument"
+    assert L.rva_status_string(-2) == b"unsupported configuration"
+    assert L.rva_status_string(-3) == b"HIP runtime error"
+    assert L.rva_status_string(99) == b"unknown status"
+    assert L.rva_version() == 100
+
+
+FAKE = ctypes.c_void_p(0x7F0000000000)  # aligned, never dereferenced: validation fails first
+MIS = ctypes.c_void_p(0x7F0000000008)   # 8-byte aligned only
+
+
+def _pack(L, B=2, N=8, H=1, d=64, dt=1, q=FAKE, mask=FAKE, qo=FAKE, cu=FAKE):
+    return L.rva_pack(q, None, None, mask, B, N, H, d, dt, qo, None, None, cu, None, None, None)
+
+
+def test_pack_validation(L):
+    assert _pack(L, mask=None) == -1 and b"mask" in L.rva_last_error()
+    assert _pack(L, B=0) == -1
+    assert _pack(L, N=0) == -1 and _pack(L, N=1025) == -1
+    assert _pack(L, H=0) == -1 and _pack(L, H=65) == -1
+    assert _pack(L, d=32) == -2 and b"head_dim" in L.rva_last_error()
+    assert _pack(L, dt=7) == -1 and b"dtype" in L.rva_last_error()
+    assert _pack(L, qo=None) == -1 and b"both" in L.rva_last_error()
+    assert _pack(L, q=MIS) == -1 and b"aligned" in L.rva_last_error()
+    assert _pack(L, cu=None) == -1 and b"cu_seqlens" in L.rva_last_error()
+    assert _pack(L, B=1 << 22, N=1024) == -1
+
+
+def test_attend_unpack_fused_validation(L):
+    f = ctypes.c_float(0.0)
+    assert L.rva_ragged_attend(FAKE, FAKE, FAKE, None, 2, 2, 64, 10, f, 1, FAKE, None) == -1
+    assert L.rva_ragged_attend(FAKE, None, FAKE, FAKE, 2, 2, 64, 10, f, 1, FAKE, None) == -1
+    assert L.rva_ragged_attend(FAKE, FAKE, FAKE, FAKE, 2, 2, 128, 10, f, 1, FAKE, None) == -2
+    assert L.rva_unpack(FAKE, FAKE, None, 2, 8, 1, 64, 1, FAKE, None) == -1
+    assert L.rva_unpack(FAKE, FAKE, FAKE, 2, 8, 1, 64, 1, MIS, None) == -1
+    assert L.rva_fused(FAKE, FAKE, FAKE, FAKE, 2, 8, 1, 64, 0, f, 1, None, None, None, None) == -1
+    assert L.rva_fused(FAKE, FAKE, FAKE, FAKE, 2, 8, 1, 64, 0, f, 3, FAKE, None, None, None) == -1
+    assert L.rva_fused(FAKE, FAKE, FAKE, FAKE, 2, 8, 1, 64, 0, f, 1, FAKE,
+                       ctypes.c_void_p(0x7F0000000002), None, None) == -1
+    assert L.rva_empty(-1, None) == -1
+
+
+def test_plan_validation(L):
+    import ragged_variable_length_amd as rva
+    d = rva._PlanDesc()
+    h = ctypes.c_void_p()
+    d.mode = 9
+    assert L.rva_plan_create(ctypes.byref(d), ctypes.byref(h)) == -1
+    assert L.rva_plan_create(None, ctypes.byref(h)) == -1
+    d.mode = rva.FUSED
+    d.B, d.N, d.H, d.d, d.dtype = 2, 8, 1, 64, 1
+    assert L.rva_plan_create(ctypes.byref(d), ctypes.byref(h)) == -1  # null pointers
+    assert h.value is None
+    assert L.rva_plan_launch(None, None) == -1
+    assert L.rva_plan_destroy(None) == 0
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    import ragged_variable_length_amd as rva
+    monkeypatch.setattr(rva, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(rva, "_lib", None)
+    with pytest.raises(ImportError):
+        rva.lib()
