@@ -1,0 +1,348 @@
+"""Benchmark of the pack -> ragged attention -> unpack path on one MI355X.
+
+Headline (the JSON line's `value`): kept tokens per second of the captured
+fused launch (one graph launch = one whole pass of the path: counts and
+offsets, row gather, attention, unpack with zero fill) on the peak-throughput
+mixed batch -- 1024 DeiT-B-shaped images, 197 tokens, 12 heads, head_dim 64,
+fp16, per-image pruning rate uniform in [0, 0.9].  Inputs are resident in
+HBM before the timed region.
+
+The same line carries, for every workload: per-call latency (host clock,
+launch + synchronise), kernel time (HIP events, warm and cache-scrubbed),
+dispatch = latency - kernel, kept tokens/s, attention TFLOP/s, algorithmic
+GB/s and the fraction of the binding roofline; the launch floor of an empty
+kernel (direct and captured); and the fp64 CPU oracle timed on this host.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
+"""
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
+MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "f32": 157.3}  # dense, published
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_mixed_b1024_traffic.json")
+KERNEL_SOURCES = ["ragged_variable_length_amd/csrc/attend.hip",
+                  "ragged_variable_length_amd/csrc/rva_device.h",
+                  "ragged_variable_length_amd/csrc/rva_internal.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def workload_stats(w):
+    """Algorithmic sizes of one pass (bytes the method must move, FLOPs)."""
+    es = 4 if w.dtype == "f32" else 2
+    R = w.H * w.d * es                    # bytes per token row
+    n = w.counts.astype("int64")
+    T = int(n.sum())
+    sum_n2 = int((n * n).sum())
+    BN = w.B * w.N
+    return {
+        "T": T,
+        "sum_n2": sum_n2,
+        "flops": 4 * w.d * w.H * sum_n2,
+        # fused: mask read, kept q/k/v rows read once, every padded O row written, offsets
+        "bytes_fused": BN + 3 * T * R + BN * R + 4 * (w.B + 2),
+        "bytes_pack": BN + 6 * T * R + 4 * T + 4 * (w.B + 2),
+        "bytes_attend": 4 * T * R + 4 * (w.B + 1),
+        "bytes_unpack": T * R + BN * R + BN + 4 * (w.B + 1),
+        "row_bytes": R,
+    }
+
+
+class Ctx:
+    def __init__(self, torch, rva, dev):
+        self.torch, self.rva, self.dev = torch, rva, dev
+        self.stream = torch.cuda.current_stream()
+        self._scrub = None
+
+    def scrub(self, i):
+        """Read 1 GiB so the next call starts with cold caches (MALL is 256 MB).
+        A read, not a write: written lines would still be draining to HBM
+        while the timed call runs."""
+        t = self.torch
+        if self._scrub is None:
+            self._scrub = t.ones(1 << 28, dtype=t.float32, device=self.dev)
+            self._sink = t.empty(1, dtype=t.float32, device=self.dev)
+        t.sum(self._scrub, dim=0, out=self._sink)
+
+    def events_time(self, fn, reps):
+        """Mean device time per call of `reps` back-to-back calls (HIP events on
+        the launch stream)."""
+        t = self.torch
+        e0, e1 = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        t.cuda.synchronize()
+        e0.record(self.stream)
+        for _ in range(reps):
+            fn()
+        e1.record(self.stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps  # us
+
+    def cold_time(self, fn, reps):
+        t = self.torch
+        out = []
+        for i in range(reps):
+            self.scrub(i)
+            e0, e1 = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+            e0.record(self.stream)
+            fn()
+            e1.record(self.stream)
+            e1.synchronize()
+            out.append(e0.elapsed_time(e1) * 1e3)
+        return statistics.median(out)
+
+    def latency(self, fn, reps):
+        """Median host time of call + synchronise (dispatch + kernel), us."""
+        t = self.torch
+        out = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            fn()
+            t.cuda.synchronize()
+            out.append((time.perf_counter() - t0) * 1e6)
+        return statistics.median(out)
+
+
+def upload(ctx, w):
+    import numpy as np
+    t = ctx.torch
+
+    def dev(x):
+        a = t.from_numpy(np.ascontiguousarray(x))
+        if w.dtype == "bf16":
+            return a.view(t.int16).to(ctx.dev).view(t.bfloat16)
+        return a.to(ctx.dev)
+    return dev(w.q), dev(w.k), dev(w.v), t.from_numpy(w.mask).to(ctx.dev)
+
+
+def make_plans(ctx, w, tensors, staged=True):
+    t, rva = ctx.torch, ctx.rva
+    q, k, v, mask = tensors
+    B, N, H, d = q.shape
+    out = t.empty_like(q)
+    cu = t.empty(B + 1, dtype=t.int32, device=ctx.dev)
+    mx = t.empty(1, dtype=t.int32, device=ctx.dev)
+    hint = int(w.counts.max())
+    plans = {"fused": rva.Plan(rva.FUSED, q=q, k=k, v=v, mask=mask, out=out, cu_seqlens=cu,
+                               max_seqlen=mx, max_seqlen_hint=hint)}
+    if staged:
+        packed = {nm: t.empty((B * N, H, d), dtype=q.dtype, device=ctx.dev) for nm in "qkvo"}
+        plans["staged"] = rva.Plan(rva.STAGED, q=q, k=k, v=v, mask=mask, out=out, packed=packed,
+                                   cu_seqlens=cu, max_seqlen=mx, max_seqlen_hint=hint)
+    return plans
+
+
+def roofline(stats, dtype, us, bytes_key):
+    gbs = stats[bytes_key] / (us * 1e-6) / 1e9
+    tfl = stats["flops"] / (us * 1e-6) / 1e12
+    t_hbm = stats[bytes_key] / (HBM_PEAK_GBS * 1e9) * 1e6
+    t_mfma = stats["flops"] / (MFMA_PEAK_TFLOPS[dtype] * 1e12) * 1e6
+    bound = "hbm" if t_hbm >= t_mfma else "mfma"
+    return {"bound": bound, "t_bound_us": round(max(t_hbm, t_mfma), 3), "GBps": round(gbs, 1),
+            "TFLOPs": round(tfl, 2), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+            "frac_mfma": round(tfl / MFMA_PEAK_TFLOPS[dtype], 4),
+            "frac": round(max(t_hbm, t_mfma) / us, 4)}
+
+
+def measure_config(ctx, w, reps, floor_us):
+    stats = workload_stats(w)
+    tensors = upload(ctx, w)
+    plans = make_plans(ctx, w, tensors)
+    res = {"workload": w.name, "B": w.B, "N": w.N, "H": w.H, "dtype": w.dtype, "T": stats["T"],
+           "gflop": round(stats["flops"] / 1e9, 4), "fused_MB": round(stats["bytes_fused"] / 1e6, 3)}
+    for name, plan in plans.items():
+        for _ in range(5):
+            plan.launch()
+        warm = ctx.events_time(plan.launch, reps)
+        cold = ctx.cold_time(plan.launch, max(5, reps // 10))
+        lat = ctx.latency(plan.launch, reps)
+        bkey = "bytes_fused" if name == "fused" else None
+        entry = {"latency_us": round(lat, 2), "kernel_us_warm": round(warm, 2),
+                 "kernel_us_cold": round(cold, 2), "dispatch_us": round(lat - cold, 2),
+                 "kept_tokens_per_s_latency": round(stats["T"] / (lat * 1e-6)),
+                 "kept_tokens_per_s_throughput": round(stats["T"] / (warm * 1e-6))}
+        if bkey:
+            entry["roofline_cold"] = roofline(stats, w.dtype, cold, bkey)
+            entry["per_call_frac"] = round(max(entry["roofline_cold"]["t_bound_us"], floor_us) / lat, 4)
+        res[name] = entry
+        plan.close()
+    # the attention kernel on its own (packed operands), cold
+    rva, t = ctx.rva, ctx.torch
+    q, k, v, mask = tensors
+    pk = rva.pack(q, k, v, mask)
+    o = t.empty_like(pk["q"])
+    mxs = int(w.counts.max())
+    att = lambda: rva.ragged_attend(pk["q"], pk["k"], pk["v"], pk["cu_seqlens"], mxs, out=o)
+    att()
+    a_us = ctx.cold_time(att, max(5, reps // 10))
+    res["attend_only"] = {"kernel_us_cold": round(a_us, 2),
+                          "roofline_cold": roofline(stats, w.dtype, a_us, "bytes_attend")}
+    return res
+
+
+def measure_floor(ctx, reps):
+    rva = ctx.rva
+    plan = rva.Plan(rva.EMPTY)
+    for _ in range(10):
+        plan.launch()
+    g_lat = ctx.latency(plan.launch, reps)
+    g_dev = ctx.events_time(plan.launch, reps)
+    d_lat = ctx.latency(lambda: rva.empty(1), reps)
+    d_dev = ctx.events_time(lambda: rva.empty(1), reps)
+    plan.close()
+    return {"graph_latency_us": round(g_lat, 2), "graph_back_to_back_us": round(g_dev, 2),
+            "direct_latency_us": round(d_lat, 2), "direct_back_to_back_us": round(d_dev, 2)}
+
+
+def cpu_baseline(w, repeats=2):
+    """The fp64 oracle, untuned, on this host: one thread (BLAS pinned to 1)."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    secs = []
+    with threadpool_limits(1):
+        for _ in range(repeats):
+            t0 = time.perf_counter()
+            oracle.pack_attend_unpack(w.q, w.k, w.v, w.mask, w.dtype)
+            secs.append(time.perf_counter() - t0)
+    s = min(secs)
+    return {"value": round(w.total_kept / s, 1), "unit": "kept tokens/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"whole {w.name} batch ({w.B} images, {w.total_kept} kept tokens), "
+                      f"pack+attend+unpack in fp64, best of {repeats} ({s:.2f} s)"}
+
+
+def load_traffic(bytes_alg):
+    """HBM bytes per fused launch from the committed rocprofv3 counter summary,
+    or None if absent or taken on a different kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    try:
+        d = json.load(open(TRAFFIC_FILE))
+    except Exception:
+        return None
+    if d.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--quick", action="store_true", help="headline only (no per-workload sweep)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--headline-only-launches", type=int, default=0,
+                    help="profiling aid: launch the headline plan this many times and exit")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the ragged path needs no cross-GPU exchange "
+              "(images shard independently), and only the one-GPU figure is reported.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import ragged_variable_length_amd as rva
+    import workloads as W
+
+    rva.lib()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    ctx = Ctx(torch, rva, dev)
+
+    log("generating the mixed batch ...")
+    w = W.mixed_peak()
+    stats = workload_stats(w)
+    tensors = upload(ctx, w)
+    plans = make_plans(ctx, w, tensors, staged=False)
+    plan = plans["fused"]
+
+    if args.headline_only_launches:
+        for _ in range(args.headline_only_launches):
+            plan.launch()
+        torch.cuda.synchronize()
+        log(f"launched {args.headline_only_launches} fused plans")
+        return
+
+    for _ in range(args.warmup):
+        plan.launch()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()  # (one process: the barrier is trivial)
+    t0 = time.perf_counter()
+    e0.record(ctx.stream)
+    for _ in range(args.steps):
+        plan.launch()
+    e1.record(ctx.stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dev_us = e0.elapsed_time(e1) * 1e3 / args.steps
+    value = stats["T"] * args.steps / wall
+    log(f"headline: {wall * 1e3 / args.steps:.3f} ms/step wall, {dev_us:.2f} us/launch (events)")
+
+    rl = roofline(stats, w.dtype, dev_us, "bytes_fused")
+    traffic = load_traffic(stats["bytes_fused"])
+    line = {
+        "metric": "ragged attention kept-tokens/s (pack->attend->unpack, one fused captured launch)",
+        "value": round(value, 1),
+        "unit": "kept tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "images": w.B, "tokens": w.N, "heads": w.H, "head_dim": w.d,
+                   "kept_tokens": stats["T"], "pruning": "per-image rate ~ U[0, 0.9]",
+                   "launch": "one captured graph of the fused kernel"},
+        "roofline": {"bound": rl["bound"], "achieved": rl["GBps"], "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": rl["frac_hbm"], "traffic": traffic,
+                     "kernel": "attend16_kernel<1,true> (fused, fp16)",
+                     "algorithmic_bytes_per_launch": stats["bytes_fused"],
+                     "avg_launch_us": round(dev_us, 3),
+                     "mfma_TFLOPs": rl["TFLOPs"], "mfma_frac": rl["frac_mfma"]},
+    }
+    for p in plans.values():
+        p.close()
+    del tensors
+
+    reps = 200
+    if not args.quick:
+        floor = measure_floor(ctx, reps)
+        line["launch_floor"] = floor
+        per = []
+        for wk in W.all_configs():
+            log(f"measuring {wk.name} ...")
+            per.append(measure_config(ctx, wk, reps if wk.B < 1024 else 50,
+                                      floor["graph_latency_us"]))
+            torch.cuda.empty_cache()
+        line["per_config"] = per
+    if not args.no_cpu:
+        log("timing the CPU oracle ...")
+        line["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

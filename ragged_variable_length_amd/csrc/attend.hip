@@ -4,27 +4,32 @@
 // Transformers" (sota2.com page, Abstract): non-causal attention over each
 // image's kept tokens only, O = softmax(Q K^T * scale) V per image and head.
 //
-// Work decomposition (CDNA4 / gfx950):
-//  * one workgroup of 8 waves per (image, head); post-pruning ViT sequences
-//    are short (at most 197 tokens at 224x224, 577 at 384x384), so one
-//    workgroup stages the whole K and V of its sequence on chip once and
-//    every wave reuses them; longer sequences are streamed in chunks;
-//  * each wave owns query blocks of 16 rows (two at a time) and walks the
-//    staged keys 32 at a time with an online softmax in fp32;
-//  * 16-bit inputs: scores are formed transposed, S^T = K Q^T, with the
-//    16x16x32 matrix-core product, so each lane ends up holding one query
-//    column and 4+4 keys -- exactly the per-lane slice the second product
-//    O^T = V^T P^T needs as its B operand.  P never leaves registers; V is
-//    staged transposed (V^T) so its A operand is two 8-byte LDS reads;
-//  * fp32 inputs use the 16x16x4 fp32 matrix-core product with the same
-//    transposed-score layout (no precision is given up for fp32 data);
-//  * row max is shared across the four lanes of a query with two xor
-//    shuffles; row sums stay per lane until the end;
+// Work decomposition (CDNA4 / gfx950), 16-bit inputs:
+//  * one workgroup of 4 waves per (image, head).  Post-pruning ViT sequences
+//    are short (at most 197 tokens at 224x224, 577 at 384x384), so the
+//    workgroup stages its sequence's V once, transposed, in LDS; longer
+//    sequences are staged in chunks;
+//  * each wave owns two query blocks of 16 rows at a time and walks the keys
+//    32 at a time;
+//  * scores are formed transposed, S^T = K Q^T, with the 16x16x32 matrix-core
+//    product: each lane then holds one query and 4+4 keys, which is exactly
+//    the per-lane slice the second product O^T = V^T P^T takes as its B
+//    operand, so P never leaves registers.  The A operand of the first
+//    product is 16 contiguous bytes of a K row, so K goes straight from
+//    memory into registers (one tile ahead of use) and needs no LDS;
+//  * softmax in fp32 with exp2 (log2 e folded into the scale).  The running
+//    max is shared by the four lanes of a query with two lane-swap steps;
+//    row sums stay per lane until the end.  The output is rescaled only when
+//    the max grows by more than 2^8 (the stale max still bounds every
+//    probability by 2^8, far inside fp16/bf16 range, and cancels exactly in
+//    the final division);
 //  * the fused form first compacts the image's keep-mask row in LDS, reads
 //    Q/K/V rows straight from the padded tensors through that list, writes
 //    O rows straight to padded positions and zero-fills pruned rows.  An
 //    optional extra workgroup computes cu_seqlens / max_seqlen in the same
 //    launch.
+// fp32 inputs use the 16x16x4 fp32 matrix-core product (no precision is
+// given up) with K and V both staged in LDS and 8-wave workgroups.
 #include <math.h>
 
 #include "rva_device.h"
@@ -63,15 +68,36 @@ struct Half16<2> {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Reductions over the four lanes l, l^16, l^32, l^48 that share a query:
+// a lane-swap exchanges 16-lane (resp. 32-lane) rows between two copies of
+// the value, after which the elementwise max/sum of the copies is the
+// reduction over the pair of rows.
+__device__ __forceinline__ float quad_max(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float quad_sum(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 __device__ __forceinline__ float max8(f32x4 a, f32x4 b) {
   return fmaxf(fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3])), fmaxf(fmaxf(b[0], b[1]), fmaxf(b[2], b[3])));
 }
 
+constexpr float kRescaleSlack = 8.0f;  // log2 units: probabilities stay <= 2^8
+
 // Online-softmax update for one 16-query block and one 32-key tile whose
 // scores are s0 (keys 4g..4g+3) and s1 (keys 16+4g..16+4g+3) in this lane.
-// Returns the probabilities in pr[8] and rescales the running state.
-__device__ __forceinline__ float softmax_step(f32x4& s0, f32x4& s1, int kvalid, float c, float& m,
-                                              float& l, float (&pr)[8]) {
+// Writes the (unnormalised) probabilities to pr[8]; rescales `o` and `l`
+// only when some query's max grew by more than kRescaleSlack.
+__device__ __forceinline__ void softmax_step(f32x4& s0, f32x4& s1, int kvalid, float c, float& m,
+                                             float& l, f32x4 (&o)[4], float (&pr)[8]) {
   const int g = lane_id() >> 4;
   if (kvalid < kKeyTile) {
 #pragma unroll
@@ -80,25 +106,32 @@ __device__ __forceinline__ float softmax_step(f32x4& s0, f32x4& s1, int kvalid, 
       if (16 + 4 * g + j >= kvalid) s1[j] = -INFINITY;
     }
   }
-  float mx = max8(s0, s1);
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float mnew = fmaxf(m, mx * c);
-  const float alpha = fast_exp2(m - mnew);
-  float sum = 0.f;
+  const float mt = quad_max(max8(s0, s1)) * c;
+  if (__any(mt > m + kRescaleSlack)) {
+    const float mnew = fmaxf(m, mt);
+    const float alpha = fast_exp2(m - mnew);
+    m = mnew;
+    l *= alpha;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    pr[j] = fast_exp2(fmaf(s0[j], c, -mnew));
-    pr[4 + j] = fast_exp2(fmaf(s1[j], c, -mnew));
+    for (int db = 0; db < 4; ++db) o[db] *= alpha;
   }
 #pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    pr[j] = fast_exp2(fmaf(s0[j], c, -m));
+    pr[4 + j] = fast_exp2(fmaf(s1[j], c, -m));
+  }
+  float sum = 0.f;
+#pragma unroll
   for (int j = 0; j < 8; ++j) sum += pr[j];
-  l = l * alpha + sum;
-  m = mnew;
-  return alpha;
+  l += sum;
 }
 
 // ---------------------------------------------------------------- 16-bit
+
+// Staged K is [kc][64] halves with the eight 16-byte pieces of row r stored
+// at piece index p ^ (r & 7): the 16 rows a b128 fragment read touches then
+// spread over all banks without padding.
+__device__ __forceinline__ int kswz(int row, int piece) { return row * 64 + ((piece ^ (row & 7)) << 3); }
 
 template <int DT>
 __device__ __forceinline__ void tile16(const typename Half16<DT>::T* __restrict__ Ks,
@@ -111,12 +144,13 @@ __device__ __forceinline__ void tile16(const typename Half16<DT>::T* __restrict_
   typedef typename Tr::V8 V8;
   typedef typename Tr::V4 V4;
   const int lane = lane_id(), g = lane >> 4, r16 = lane & 15;
+  // A operand of S^T = K Q^T: lane (r16, g) holds K[k0 + 16 kb + r16][32 ks + 8 g .. + 7]
   V8 kf[2][2];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
-      kf[kb][ks] = *reinterpret_cast<const V8*>(Ks + (k0 + kb * 16 + r16) * kKPitch16 + ks * 32 + g * 8);
+      kf[kb][ks] = *reinterpret_cast<const V8*>(Ks + kswz(k0 + kb * 16 + r16, ks * 4 + g));
   V8 vf[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) {
@@ -134,52 +168,75 @@ __device__ __forceinline__ void tile16(const typename Half16<DT>::T* __restrict_
     s0 = Tr::mfma(kf[0][1], qf[i][1], s0);
     s1 = Tr::mfma(kf[1][1], qf[i][1], s1);
     float pr[8];
-    const float alpha = softmax_step(s0, s1, kvalid, c, m[i], l[i], pr);
+    softmax_step(s0, s1, kvalid, c, m[i], l[i], o[i], pr);
     V8 pf;
 #pragma unroll
     for (int j = 0; j < 8; ++j) pf[j] = (T)pr[j];
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      o[i][db] *= alpha;
-      o[i][db] = Tr::mfma(vf[db], pf, o[i][db]);
-    }
+    for (int db = 0; db < 4; ++db) o[i][db] = Tr::mfma(vf[db], pf, o[i][db]);
   }
 }
 
-// Stage keys [c0, c0 + rows) of the sequence: K rows as they are, V
-// transposed.  V columns [rows, round_up(rows, 32)) are zeroed so masked
-// probabilities (exact zeros) never meet stale LDS contents.
+// Stage keys [c0, c0 + rows) of the sequence: K rows into Ks (swizzled
+// 16-byte pieces), V transposed into Vt[d][key].  Every global load of the
+// chunk is issued before the first LDS store, so one memory round trip
+// stages the whole chunk.  The V^T block of an item is 4 keys x 4 dims: four
+// 8-byte row loads (16 lanes cover one 128-byte row), a 4x4 transpose of
+// 16-bit values in registers, four 8-byte LDS stores.  Rows/columns
+// [rows, round_up(rows, 32)) are zeroed so masked probabilities (exact
+// zeros) never meet stale LDS contents.
 template <int DT, typename Elem>
 __device__ __forceinline__ void stage16(const typename Half16<DT>::T* __restrict__ kg,
                                         const typename Half16<DT>::T* __restrict__ vg,
-                                        typename Half16<DT>::T* Ks, typename Half16<DT>::T* Vt, int VP,
-                                        int c0, int rows, Elem elem) {
+                                        typename Half16<DT>::T* Ks, typename Half16<DT>::T* Vt,
+                                        int VP, int c0, int rows, Elem elem) {
   typedef typename Half16<DT>::T T;
+  constexpr int NT = kAttnThreads16;
+  constexpr int UK = kKcMax16 * 8 / NT;         // K pieces per thread at most
+  constexpr int UV = kKcMax16 / 4 * 16 / NT;    // V^T blocks per thread at most
   const int tid = threadIdx.x;
-  const int total = round_up(rows, kKeyTile) * 8;  // 16-byte pieces, <= kKcMax16 * 8
-  u32x4 kr[4], vr[4];
+  const int rpad = round_up(rows, kKeyTile);
+  const int kitems = rpad * 8, vitems = rpad / 4 * 16;
+  u32x4 kr[UK];
+  u32x2 vr[UV][4];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int e = tid + u * kAttnThreads;
-    kr[u] = u32x4{0u, 0u, 0u, 0u};
-    vr[u] = kr[u];
+  for (int u = 0; u < UK; ++u) {
+    const int e = tid + u * NT;
     const int r = e >> 3, pc = e & 7;
-    if (e < total && r < rows) {
-      const size_t el = elem(c0 + r) + pc * 8;
-      kr[u] = *reinterpret_cast<const u32x4*>(kg + el);
-      vr[u] = *reinterpret_cast<const u32x4*>(vg + el);
+    kr[u] = u32x4{0u, 0u, 0u, 0u};
+    if (e < kitems && r < rows) kr[u] = *reinterpret_cast<const u32x4*>(kg + elem(c0 + r) + pc * 8);
+  }
+#pragma unroll
+  for (int u = 0; u < UV; ++u) {
+    const int it = tid + u * NT;
+    const int kq = it >> 4, dq = it & 15;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int key = 4 * kq + j;
+      vr[u][j] = u32x2{0u, 0u};
+      if (it < vitems && key < rows) vr[u][j] = *reinterpret_cast<const u32x2*>(vg + elem(c0 + key) + 4 * dq);
     }
   }
-  uint16_t* vt16 = reinterpret_cast<uint16_t*>(Vt);
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int e = tid + u * kAttnThreads;
-    if (e < total) {
-      const int r = e >> 3, pc = e & 7;
-      *reinterpret_cast<u32x4*>(Ks + r * kKPitch16 + pc * 8) = kr[u];
+  for (int u = 0; u < UK; ++u) {
+    const int e = tid + u * NT;
+    if (e < kitems) *reinterpret_cast<u32x4*>(Ks + kswz(e >> 3, e & 7)) = kr[u];
+  }
+  char* vt = reinterpret_cast<char*>(Vt);
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        vt16[(pc * 8 + i) * VP + r] = (uint16_t)(vr[u][i >> 1] >> (16 * (i & 1)));
+  for (int u = 0; u < UV; ++u) {
+    const int it = tid + u * NT;
+    if (it >= vitems) continue;
+    const int kq = it >> 4, dq = it & 15;
+    // vr[u][j] holds V[key 4kq+j][dims 4dq..4dq+3]; out holds V^T[dim 4dq+i][keys 4kq..4kq+3]
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int w = i >> 1;
+      const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;  // high or low halves
+      u32x2 out;
+      out[0] = __builtin_amdgcn_perm(vr[u][1][w], vr[u][0][w], sel);
+      out[1] = __builtin_amdgcn_perm(vr[u][3][w], vr[u][2][w], sel);
+      *reinterpret_cast<u32x2*>(vt + ((size_t)(4 * dq + i) * VP + 4 * kq) * 2) = out;
     }
   }
 }
@@ -194,12 +251,12 @@ __device__ __forceinline__ void attend_seq16(const AttnParams& p, int n, unsigne
   const int lane = lane_id(), w = wave_id(), g = lane >> 4, r16 = lane & 15;
   const int kc = p.kc, VP = kc + kVPad16;
   T* Ks = reinterpret_cast<T*>(kvbase);
-  T* Vt = Ks + kc * kKPitch16;
+  T* Vt = Ks + kc * kHeadDim;
   const T* __restrict__ qg = static_cast<const T*>(p.q);
   const T* __restrict__ kg = static_cast<const T*>(p.k);
   const T* __restrict__ vg = static_cast<const T*>(p.v);
   T* __restrict__ og = static_cast<T*>(p.o);
-  constexpr int kWaves = kAttnThreads / 64;
+  constexpr int kWaves = kAttnThreads16 / 64;
   constexpr int kPerPass = kWaves * kQBlocksPerWave;
   const int nqb = (n + kQBlock - 1) / kQBlock;
   const int npass = (nqb + kPerPass - 1) / kPerPass;
@@ -216,10 +273,6 @@ __device__ __forceinline__ void attend_seq16(const AttnParams& p, int n, unsigne
     for (int i = 0; i < 2; ++i) {
       qb[i] = pass * kPerPass + w + i * kWaves;
       act[i] = qb[i] < nqb;
-      m[i] = -INFINITY;
-      l[i] = 0.f;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) o[i][db] = f32x4{0.f, 0.f, 0.f, 0.f};
       const int q = qb[i] * kQBlock + r16;
       qf[i][0] = V8{};
       qf[i][1] = V8{};
@@ -229,13 +282,25 @@ __device__ __forceinline__ void attend_seq16(const AttnParams& p, int n, unsigne
         qf[i][1] = *reinterpret_cast<const V8*>(qg + e + 32 + 8 * g);
       }
     }
-    for (int ch = 0; ch < nchunk; ++ch) {
+    for (int cc = 0; cc < nchunk; ++cc) {
+      // odd passes walk the chunks backwards so the chunk left staged by the
+      // previous pass is used first (softmax accumulation is order-free)
+      const int ch = (pass & 1) ? nchunk - 1 - cc : cc;
       const int c0 = ch * kc;
       const int rows = min(kc, n - c0);
-      if (nchunk > 1 || pass == 0) {
-        if (pass > 0 || ch > 0) __syncthreads();
+      if (!(pass > 0 && cc == 0)) {
+        if (pass > 0 || cc > 0) __syncthreads();
         stage16<DT>(kg, vg, Ks, Vt, VP, c0, rows, elem);
         __syncthreads();
+      }
+      if (cc == 0) {  // accumulators come alive only after the first staging
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          m[i] = -INFINITY;
+          l[i] = 0.f;
+#pragma unroll
+          for (int db = 0; db < 4; ++db) o[i][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
       }
       if (act[0]) {
         const int ntile = (rows + kKeyTile - 1) / kKeyTile;
@@ -248,10 +313,7 @@ __device__ __forceinline__ void attend_seq16(const AttnParams& p, int n, unsigne
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       if (!act[i]) continue;
-      float lt = l[i];
-      lt += __shfl_xor(lt, 16);
-      lt += __shfl_xor(lt, 32);
-      const float inv = 1.f / lt;
+      const float inv = 1.f / quad_sum(l[i]);
       const int q = qb[i] * kQBlock + r16;
       if (q < n) {
         const size_t e = elem(q);
@@ -305,25 +367,24 @@ __device__ __forceinline__ void tile32(const float* __restrict__ Ks, const float
       s1 = mfma_f32(kf[1][t >> 2][t & 3], qf[i][t >> 2][t & 3], s1);
     }
     float pr[8];
-    const float alpha = softmax_step(s0, s1, kvalid, c, m[i], l[i], pr);
+    softmax_step(s0, s1, kvalid, c, m[i], l[i], o[i], pr);
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      o[i][db] *= alpha;
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int j = 0; j < 8; ++j) o[i][db] = mfma_f32(va[db][j], pr[j], o[i][db]);
-    }
   }
 }
 
 template <typename Elem>
 __device__ __forceinline__ void stage32(const float* __restrict__ kg, const float* __restrict__ vg,
                                         float* Ks, float* Vs, int c0, int rows, Elem elem) {
+  constexpr int NT = kAttnThreads32;
   const int tid = threadIdx.x;
   const int total = round_up(rows, kKeyTile) * 16;  // <= kKcMax32 * 16
   u32x4 kr[4], vr[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    const int e = tid + u * kAttnThreads;
+    const int e = tid + u * NT;
     kr[u] = u32x4{0u, 0u, 0u, 0u};
     vr[u] = kr[u];
     const int r = e >> 4, pc = e & 15;
@@ -335,7 +396,7 @@ __device__ __forceinline__ void stage32(const float* __restrict__ kg, const floa
   }
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    const int e = tid + u * kAttnThreads;
+    const int e = tid + u * NT;
     if (e < total) {
       const int r = e >> 4, pc = e & 15;
       *reinterpret_cast<u32x4*>(Ks + r * kPitch32 + pc * 4) = kr[u];
@@ -355,7 +416,7 @@ __device__ __forceinline__ void attend_seq32(const AttnParams& p, int n, unsigne
   const float* __restrict__ kg = static_cast<const float*>(p.k);
   const float* __restrict__ vg = static_cast<const float*>(p.v);
   float* __restrict__ og = static_cast<float*>(p.o);
-  constexpr int kWaves = kAttnThreads / 64;
+  constexpr int kWaves = kAttnThreads32 / 64;
   constexpr int kPerPass = kWaves * kQBlocksPerWave;
   const int nqb = (n + kQBlock - 1) / kQBlock;
   const int npass = (nqb + kPerPass - 1) / kPerPass;
@@ -404,10 +465,7 @@ __device__ __forceinline__ void attend_seq32(const AttnParams& p, int n, unsigne
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       if (!act[i]) continue;
-      float lt = l[i];
-      lt += __shfl_xor(lt, 16);
-      lt += __shfl_xor(lt, 32);
-      const float inv = 1.f / lt;
+      const float inv = 1.f / quad_sum(l[i]);
       const int q = qb[i] * kQBlock + r16;
       if (q < n) {
         const size_t e = elem(q);
@@ -422,13 +480,13 @@ __device__ __forceinline__ void attend_seq32(const AttnParams& p, int n, unsigne
 // ---------------------------------------------------------------- kernels
 
 // Zero the output rows of pruned tokens of image b, head h (fused form).
-template <int ESIZE>
+template <int NT, int ESIZE>
 __device__ __forceinline__ void zero_pruned(void* o, const uint64_t* ballots, int b, int N, int H,
                                             int h) {
   constexpr int PIECES = kHeadDim * ESIZE / 16;
   const int total = N * PIECES;
   char* base = static_cast<char*>(o);
-  for (int e = threadIdx.x; e < total; e += kAttnThreads) {
+  for (int e = threadIdx.x; e < total; e += NT) {
     const int j = e / PIECES, pc = e - j * PIECES;
     const bool kept = (ballots[j >> 6] >> (j & 63)) & 1ull;
     if (!kept)
@@ -438,14 +496,13 @@ __device__ __forceinline__ void zero_pruned(void* o, const uint64_t* ballots, in
 }
 
 template <int DT, bool FUSED>
-__global__ __launch_bounds__(kAttnThreads) void attend_kernel(AttnParams p) {
-  extern __shared__ __align__(16) unsigned char smem[];
+__device__ __forceinline__ void attend_body(const AttnParams& p, unsigned char* smem) {
+  constexpr int NT = DT == 0 ? kAttnThreads32 : kAttnThreads16;
   int bid = blockIdx.x;
   if constexpr (FUSED) {
     if (p.cu_out || p.max_out) {
       if (bid == 0) {
-        count_scan_block<kAttnThreads>(p.mask, p.B, p.N, p.cu_out, p.max_out,
-                                       reinterpret_cast<int*>(smem));
+        count_scan_block<NT>(p.mask, p.B, p.N, p.cu_out, p.max_out, reinterpret_cast<int*>(smem));
         return;
       }
       --bid;
@@ -458,8 +515,8 @@ __global__ __launch_bounds__(kAttnThreads) void attend_kernel(AttnParams p) {
     const size_t off = (size_t)round_up(N * 4, 16);
     uint64_t* ballots = reinterpret_cast<uint64_t*>(smem + off);
     int32_t* cnt = reinterpret_cast<int32_t*>(smem + off + 16 * 8);
-    const int n = compact_row<kAttnThreads>(p.mask + (size_t)b * N, N, idx, nullptr, ballots, cnt);
-    zero_pruned<DT == 0 ? 4 : 2>(p.o, ballots, b, N, H, h);
+    const int n = compact_row<NT>(p.mask + (size_t)b * N, N, idx, nullptr, ballots, cnt);
+    zero_pruned<NT, DT == 0 ? 4 : 2>(p.o, ballots, b, N, H, h);
     if (n <= 0) return;
     unsigned char* kvbase = smem + attn_compact_bytes(N);
     auto elem = [=](int r) -> size_t { return (((size_t)b * N + idx[r]) * H + h) * kHeadDim; };
@@ -479,38 +536,50 @@ __global__ __launch_bounds__(kAttnThreads) void attend_kernel(AttnParams p) {
   }
 }
 
+// 16-bit: 4 waves, register budget for 3 waves per SIMD (3 workgroups per CU).
 template <int DT, bool FUSED>
-static hipError_t set_lds_limit() {
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(&attend_kernel<DT, FUSED>),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+__global__ __launch_bounds__(kAttnThreads16, 3) void attend16_kernel(AttnParams p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  attend_body<DT, FUSED>(p, smem);
+}
+
+template <bool FUSED>
+__global__ __launch_bounds__(kAttnThreads32) void attend32_kernel(AttnParams p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  attend_body<0, FUSED>(p, smem);
+}
+
+static hipError_t set_lds_limit(const void* fn) {
+  return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
 }
 
 hipError_t attend_init() {
-  hipError_t e;
-  if ((e = set_lds_limit<0, false>()) != hipSuccess) return e;
-  if ((e = set_lds_limit<1, false>()) != hipSuccess) return e;
-  if ((e = set_lds_limit<2, false>()) != hipSuccess) return e;
-  if ((e = set_lds_limit<0, true>()) != hipSuccess) return e;
-  if ((e = set_lds_limit<1, true>()) != hipSuccess) return e;
-  return set_lds_limit<2, true>();
-}
-
-template <int DT, bool FUSED>
-static void launch_one(const AttnParams& p, int grid, size_t lds, hipStream_t s) {
-  hipLaunchKernelGGL((attend_kernel<DT, FUSED>), dim3(grid), dim3(kAttnThreads), lds, s, p);
+  const void* fns[6] = {reinterpret_cast<const void*>(&attend32_kernel<false>),
+                        reinterpret_cast<const void*>(&attend32_kernel<true>),
+                        reinterpret_cast<const void*>(&attend16_kernel<1, false>),
+                        reinterpret_cast<const void*>(&attend16_kernel<1, true>),
+                        reinterpret_cast<const void*>(&attend16_kernel<2, false>),
+                        reinterpret_cast<const void*>(&attend16_kernel<2, true>)};
+  for (const void* f : fns) {
+    hipError_t e = set_lds_limit(f);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_attend(const AttnParams& p, int dtype, bool fused, hipStream_t s) {
   const size_t lds = attn_lds_bytes(dtype, fused, p.N, p.kc);
   const int grid = p.B * p.H + ((fused && (p.cu_out || p.max_out)) ? 1 : 0);
-  if (fused) {
-    if (dtype == 0) launch_one<0, true>(p, grid, lds, s);
-    else if (dtype == 1) launch_one<1, true>(p, grid, lds, s);
-    else launch_one<2, true>(p, grid, lds, s);
+  const dim3 blk(attn_threads(dtype));
+  if (dtype == 0) {
+    if (fused) hipLaunchKernelGGL((attend32_kernel<true>), dim3(grid), blk, lds, s, p);
+    else hipLaunchKernelGGL((attend32_kernel<false>), dim3(grid), blk, lds, s, p);
+  } else if (dtype == 1) {
+    if (fused) hipLaunchKernelGGL((attend16_kernel<1, true>), dim3(grid), blk, lds, s, p);
+    else hipLaunchKernelGGL((attend16_kernel<1, false>), dim3(grid), blk, lds, s, p);
   } else {
-    if (dtype == 0) launch_one<0, false>(p, grid, lds, s);
-    else if (dtype == 1) launch_one<1, false>(p, grid, lds, s);
-    else launch_one<2, false>(p, grid, lds, s);
+    if (fused) hipLaunchKernelGGL((attend16_kernel<2, true>), dim3(grid), blk, lds, s, p);
+    else hipLaunchKernelGGL((attend16_kernel<2, false>), dim3(grid), blk, lds, s, p);
   }
   return hipGetLastError();
 }

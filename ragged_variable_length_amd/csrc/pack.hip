@@ -16,7 +16,7 @@ __global__ __launch_bounds__(kScanThreads) void count_scan_kernel(const uint8_t*
                                                                   int B, int N,
                                                                   int32_t* __restrict__ cu,
                                                                   int32_t* __restrict__ max_out) {
-  __shared__ int lds[kScanThreads + 64];
+  __shared__ int lds[4 * kScanThreads + 64];
   count_scan_block<kScanThreads>(mask, B, N, cu, max_out, lds);
 }
 

@@ -76,36 +76,100 @@ __device__ int block_max(int v, int* tmp) {
   return m;
 }
 
+// Bit i of the result is set when byte i of the 16-byte chunk is nonzero.
+__device__ __forceinline__ uint32_t nonzero_bytes16(u32x4 v) {
+  uint32_t out = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t x = v[k];
+    // high bit of each byte set iff the byte is nonzero
+    const uint32_t hi = (((x & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | x) & 0x80808080u;
+    // gather the four high bits into a nibble (no carries: distinct bit positions)
+    out |= ((((hi >> 7) * 0x00204081u) >> 21) & 0xFu) << (4 * k);
+  }
+  return out;
+}
+
 // Kept counts of every image and their exclusive prefix (cu_seqlens), plus
 // the largest count, computed by ONE workgroup of NT threads.  Images are
-// taken NT at a time: each wave counts whole mask rows (lanes stride the
-// row), then the workgroup scans the NT counts and carries the total into
-// the next group.  `lds` holds at least NT + 64 ints.
+// taken SEG = 4 * NT at a time.  The segment's mask bytes are read as a flat
+// array of 16-byte chunks (all threads, several chunks in flight each); a
+// chunk straddles at most one image boundary when N >= 16, and its nonzero
+// bytes are credited to the (one or two) images with LDS atomics.  The
+// workgroup then scans the SEG counts (4 per thread) and carries the total
+// into the next segment.  `lds` holds at least SEG + 64 ints.
 template <int NT>
-__device__ void count_scan_block(const uint8_t* __restrict__ mask, int B, int N,
+__device__ __forceinline__ void count_scan_block(const uint8_t* __restrict__ mask, int B, int N,
                                  int32_t* __restrict__ cu, int32_t* __restrict__ max_out,
                                  int* lds) {
-  constexpr int W = NT / 64;
-  const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
+  constexpr int SEG = 4 * NT;
+  const int tid = threadIdx.x;
   int* cnt = lds;
-  int* tmp = lds + NT;
+  int* tmp = lds + SEG;
   if (tid == 0 && cu) cu[0] = 0;
+  const bool vec = N >= 16 && (reinterpret_cast<uintptr_t>(mask) & 15) == 0;
+  const long long total_bytes = (long long)B * N;
   int carry = 0, mx = 0;
-  for (int base = 0; base < B; base += NT) {
-    const int nimg = min(NT, B - base);
-    for (int i = w; i < nimg; i += W) {
-      const uint8_t* row = mask + (size_t)(base + i) * N;
-      int c = 0;
-      for (int j = lane; j < N; j += 64) c += row[j] != 0;
-      c = wave_sum(c);
-      if (lane == 0) cnt[i] = c;
+  for (int b0 = 0; b0 < B; b0 += SEG) {
+    const int nimg = min(SEG, B - b0);
+    for (int i = tid; i < SEG; i += NT) cnt[i] = 0;
+    __syncthreads();
+    const long long lo = (long long)b0 * N, hi = (long long)(b0 + nimg) * N;
+    if (vec) {
+      // whole 16-byte chunks that lie inside [0, B*N): chunk c covers flat
+      // bytes [16c, 16c + 16); bytes outside [lo, hi) are ignored
+      const long long c_lo = lo >> 4;
+      const long long c_hi = min((hi + 15) >> 4, total_bytes >> 4);
+      for (long long c0 = c_lo + tid; c0 < c_hi; c0 += 4 * NT) {
+        u32x4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const long long c = c0 + (long long)u * NT;
+          v[u] = c < c_hi ? *reinterpret_cast<const u32x4*>(mask + 16 * c) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const long long c = c0 + (long long)u * NT;
+          if (c >= c_hi) continue;
+          uint32_t bits = nonzero_bytes16(v[u]);
+          const long long f = 16 * c;  // flat index of byte 0
+          if (f < lo) bits &= 0xFFFFu << (int)(lo - f);
+          if (f + 16 > hi) bits &= 0xFFFFu >> (int)(f + 16 - hi);
+          const int img = (int)(f / N);               // image of byte 0
+          const int split = (int)((long long)(img + 1) * N - f);  // bytes of byte 0's image
+          const uint32_t first = split >= 16 ? bits : bits & ((1u << split) - 1u);
+          const uint32_t rest = bits ^ first;
+          if (first) atomicAdd(&cnt[img - b0 < 0 ? 0 : img - b0], __popc(first));
+          if (rest) atomicAdd(&cnt[img + 1 - b0], __popc(rest));
+        }
+      }
+      // bytes of a final partial chunk (B*N not a multiple of 16)
+      for (long long j = max(lo, (total_bytes >> 4) << 4) + tid; j < hi; j += NT)
+        if (mask[j]) atomicAdd(&cnt[(int)(j / N) - b0], 1);
+    } else {
+      for (long long j = lo + tid; j < hi; j += NT)
+        if (mask[j]) atomicAdd(&cnt[(int)(j / N) - b0], 1);
     }
     __syncthreads();
-    const int v = tid < nimg ? cnt[tid] : 0;
+    // scan: thread t owns counts 4t..4t+3
+    int v4[4], s = 0, m4 = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int i = 4 * tid + k;
+      v4[k] = i < nimg ? cnt[i] : 0;
+      s += v4[k];
+      m4 = max(m4, v4[k]);
+    }
     int total;
-    const int incl = block_inclusive_scan<NT>(v, tmp, &total);
-    if (cu && tid < nimg) cu[base + tid + 1] = carry + incl;
-    mx = max(mx, block_max<NT>(v, tmp));
+    const int incl = block_inclusive_scan<NT>(s, tmp, &total);
+    int run = carry + incl - s;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int i = 4 * tid + k;
+      run += v4[k];
+      if (cu && i < nimg) cu[b0 + i + 1] = run;
+    }
+    mx = max(mx, block_max<NT>(m4, tmp));
     carry += total;
   }
   if (tid == 0 && max_out) *max_out = mx;

@@ -9,18 +9,19 @@
 namespace rva {
 
 constexpr int kHeadDim = 64;
-constexpr int kAttnThreads = 512;   // 8 waves of 64 lanes per attention workgroup
+constexpr int kAttnThreads16 = 256; // 4 waves per attention workgroup (16-bit inputs)
+constexpr int kAttnThreads32 = 512; // 8 waves per attention workgroup (fp32 inputs)
 constexpr int kQBlock = 16;         // query rows per matrix-core block
 constexpr int kQBlocksPerWave = 2;  // query blocks a wave carries through one pass
 constexpr int kKeyTile = 32;        // keys per inner step
 constexpr int kPackThreads = 256;
 constexpr int kScanThreads = 1024;
 
-// Keys staged on chip per chunk.  16-bit: K rows [kc][72] + V^T [64][kc + 8]
-// halves; fp32: K and V rows [kc][68] floats.
-constexpr int kKcMax16 = 256;
+// Keys staged on chip per chunk.  16-bit: K rows [kc][64] halves (16-byte
+// pieces XOR-swizzled by row) + V^T [64][kc + 8] halves; fp32: K and V rows
+// [kc][68] floats.
+constexpr int kKcMax16 = 128;
 constexpr int kKcMax32 = 128;
-constexpr int kKPitch16 = 72;  // halves per staged K row (64 + 8 pad: keeps 16 B alignment)
 constexpr int kVPad16 = 8;     // halves of pad per staged V^T row
 constexpr int kPitch32 = 68;   // floats per staged K/V row for fp32
 
@@ -58,11 +59,13 @@ __host__ __device__ inline size_t attn_compact_bytes(int N) {
   return (size_t)round_up(N * 4, 16) + 16 * 8 + 16 * 4;
 }
 
+inline int attn_threads(int dtype) { return dtype == 0 ? kAttnThreads32 : kAttnThreads16; }
+
 inline size_t attn_lds_bytes(int dtype, bool fused, int N, int kc) {
   size_t kv = dtype == 0 ? (size_t)kc * kPitch32 * 4 * 2
-                         : (size_t)kc * kKPitch16 * 2 + (size_t)kHeadDim * (kc + kVPad16) * 2;
+                         : (size_t)kc * kHeadDim * 2 + (size_t)kHeadDim * (kc + kVPad16) * 2;
   size_t head = fused ? attn_compact_bytes(N) : 0;
-  size_t scan = (size_t)(kAttnThreads + 64) * 4;  // fused scan workgroup reuses LDS
+  size_t scan = (size_t)(4 * attn_threads(dtype) + 64) * 4;  // fused scan workgroup reuses LDS
   size_t total = head + kv;
   return total > scan ? total : scan;
 }
