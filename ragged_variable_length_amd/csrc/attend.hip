@@ -126,6 +126,34 @@ __device__ __forceinline__ void softmax_step(f32x4& s0, f32x4& s1, int kvalid, f
   l += sum;
 }
 
+// 16-bit variant: the row sums are a fifth accumulator block o[4] (computed
+// by the matrix cores from an all-ones operand), so only the max is tracked
+// here; a rescale multiplies all five blocks.
+__device__ __forceinline__ void softmax_step16(f32x4& s0, f32x4& s1, int kvalid, float c, float& m,
+                                               f32x4 (&o)[5], float (&pr)[8]) {
+  const int g = lane_id() >> 4;
+  if (kvalid < kKeyTile) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (4 * g + j >= kvalid) s0[j] = -INFINITY;
+      if (16 + 4 * g + j >= kvalid) s1[j] = -INFINITY;
+    }
+  }
+  const float mt = quad_max(max8(s0, s1)) * c;
+  if (__any(mt > m + kRescaleSlack)) {
+    const float mnew = fmaxf(m, mt);
+    const float alpha = fast_exp2(m - mnew);
+    m = mnew;
+#pragma unroll
+    for (int db = 0; db < 5; ++db) o[db] *= alpha;
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    pr[j] = fast_exp2(fmaf(s0[j], c, -m));
+    pr[4 + j] = fast_exp2(fmaf(s1[j], c, -m));
+  }
+}
+
 // ---------------------------------------------------------------- 16-bit
 
 // Staged K is [kc][64] halves with the eight 16-byte pieces of row r stored
@@ -137,8 +165,7 @@ template <int DT>
 __device__ __forceinline__ void tile16(const typename Half16<DT>::T* __restrict__ Ks,
                                        const typename Half16<DT>::T* __restrict__ Vt, int VP, int k0,
                                        int kvalid, const typename Half16<DT>::V8 (&qf)[2][2],
-                                       f32x4 (&o)[2][4], float (&m)[2], float (&l)[2], bool two,
-                                       float c) {
+                                       f32x4 (&o)[2][5], float (&m)[2], bool two, float c) {
   typedef Half16<DT> Tr;
   typedef typename Tr::T T;
   typedef typename Tr::V8 V8;
@@ -168,32 +195,48 @@ __device__ __forceinline__ void tile16(const typename Half16<DT>::T* __restrict_
     s0 = Tr::mfma(kf[0][1], qf[i][1], s0);
     s1 = Tr::mfma(kf[1][1], qf[i][1], s1);
     float pr[8];
-    softmax_step(s0, s1, kvalid, c, m[i], l[i], o[i], pr);
+    softmax_step16(s0, s1, kvalid, c, m[i], o[i], pr);
     V8 pf;
 #pragma unroll
     for (int j = 0; j < 8; ++j) pf[j] = (T)pr[j];
 #pragma unroll
     for (int db = 0; db < 4; ++db) o[i][db] = Tr::mfma(vf[db], pf, o[i][db]);
+    // row sums of the rounded probabilities: every row of an all-ones A
+    // operand yields sum_k P[q][k], so each lane ends up holding its query's sum
+    V8 ones;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ones[j] = (T)1.0f;
+    o[i][4] = Tr::mfma(ones, pf, o[i][4]);
   }
 }
 
+// Global accesses of the 16-bit path go through raw buffer descriptors whose
+// base is the sequence's head slice and whose size covers exactly its rows:
+// offsets are 32-bit, and an offset past the end (kOOB) reads zeros and
+// drops stores in hardware, so ragged tails need no branches.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format (gfx9 family)
+constexpr uint32_t kOOB = 0x80000000u;   // beyond any descriptor size used here
+
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRsrcWord3);
+}
+
 // Stage keys [c0, c0 + rows) of the sequence: K rows into Ks (swizzled
-// 16-byte pieces), V transposed into Vt[d][key].  Every global load of the
-// chunk is issued before the first LDS store, so one memory round trip
-// stages the whole chunk.  The V^T block of an item is 4 keys x 4 dims: four
-// 8-byte row loads (16 lanes cover one 128-byte row), a 4x4 transpose of
-// 16-bit values in registers, four 8-byte LDS stores.  Rows/columns
-// [rows, round_up(rows, 32)) are zeroed so masked probabilities (exact
-// zeros) never meet stale LDS contents.
-template <int DT, typename Elem>
-__device__ __forceinline__ void stage16(const typename Half16<DT>::T* __restrict__ kg,
-                                        const typename Half16<DT>::T* __restrict__ vg,
-                                        typename Half16<DT>::T* Ks, typename Half16<DT>::T* Vt,
-                                        int VP, int c0, int rows, Elem elem) {
-  typedef typename Half16<DT>::T T;
+// 16-byte pieces), V transposed into Vt[d][key].  Every load of the chunk is
+// issued before the first LDS store, so one memory round trip stages the
+// whole chunk.  The V^T block of an item is 4 keys x 4 dims: four 8-byte row
+// loads (16 lanes cover one 128-byte row), a 4x4 transpose of 16-bit values
+// in registers, four 8-byte LDS stores.  Keys in [rows, round_up(rows, 32))
+// load as zeros, so masked probabilities (exact zeros) never meet stale LDS
+// contents.  `roff(r)` is the byte offset of sequence row r.
+template <int DT, typename RowOff>
+__device__ __forceinline__ void stage16(Rsrc rk, Rsrc rv, typename Half16<DT>::T* Ks,
+                                        typename Half16<DT>::T* Vt, int VP, int c0, int rows,
+                                        RowOff roff) {
   constexpr int NT = kAttnThreads16;
-  constexpr int UK = kKcMax16 * 8 / NT;         // K pieces per thread at most
-  constexpr int UV = kKcMax16 / 4 * 16 / NT;    // V^T blocks per thread at most
+  constexpr int UK = kKcMax16 * 8 / NT;       // K pieces per thread at most
+  constexpr int UV = kKcMax16 / 4 * 16 / NT;  // V^T blocks per thread at most
   const int tid = threadIdx.x;
   const int rpad = round_up(rows, kKeyTile);
   const int kitems = rpad * 8, vitems = rpad / 4 * 16;
@@ -203,8 +246,8 @@ __device__ __forceinline__ void stage16(const typename Half16<DT>::T* __restrict
   for (int u = 0; u < UK; ++u) {
     const int e = tid + u * NT;
     const int r = e >> 3, pc = e & 7;
-    kr[u] = u32x4{0u, 0u, 0u, 0u};
-    if (e < kitems && r < rows) kr[u] = *reinterpret_cast<const u32x4*>(kg + elem(c0 + r) + pc * 8);
+    const uint32_t o = (e < kitems && r < rows) ? roff(c0 + r) + pc * 16 : kOOB;
+    kr[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)o, 0, 0);
   }
 #pragma unroll
   for (int u = 0; u < UV; ++u) {
@@ -213,8 +256,8 @@ __device__ __forceinline__ void stage16(const typename Half16<DT>::T* __restrict
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int key = 4 * kq + j;
-      vr[u][j] = u32x2{0u, 0u};
-      if (it < vitems && key < rows) vr[u][j] = *reinterpret_cast<const u32x2*>(vg + elem(c0 + key) + 4 * dq);
+      const uint32_t o = (it < vitems && key < rows) ? roff(c0 + key) + dq * 8 : kOOB;
+      vr[u][j] = __builtin_amdgcn_raw_buffer_load_b64(rv, (int)o, 0, 0);
     }
   }
 #pragma unroll
@@ -236,14 +279,16 @@ __device__ __forceinline__ void stage16(const typename Half16<DT>::T* __restrict
       u32x2 out;
       out[0] = __builtin_amdgcn_perm(vr[u][1][w], vr[u][0][w], sel);
       out[1] = __builtin_amdgcn_perm(vr[u][3][w], vr[u][2][w], sel);
-      *reinterpret_cast<u32x2*>(vt + ((size_t)(4 * dq + i) * VP + 4 * kq) * 2) = out;
+      *reinterpret_cast<u32x2*>(vt + ((4 * dq + i) * VP + 4 * kq) * 2) = out;
     }
   }
 }
 
-template <int DT, typename Elem>
+// One sequence (image or packed run), one head.  rq/rk/rv/ro cover the
+// sequence's head slice; roff(r) is the byte offset of its row r.
+template <int DT, typename RowOff>
 __device__ __forceinline__ void attend_seq16(const AttnParams& p, int n, unsigned char* kvbase,
-                                             Elem elem) {
+                                             Rsrc rq, Rsrc rk, Rsrc rv, Rsrc ro, RowOff roff) {
   typedef Half16<DT> Tr;
   typedef typename Tr::T T;
   typedef typename Tr::V8 V8;
@@ -252,10 +297,6 @@ __device__ __forceinline__ void attend_seq16(const AttnParams& p, int n, unsigne
   const int kc = p.kc, VP = kc + kVPad16;
   T* Ks = reinterpret_cast<T*>(kvbase);
   T* Vt = Ks + kc * kHeadDim;
-  const T* __restrict__ qg = static_cast<const T*>(p.q);
-  const T* __restrict__ kg = static_cast<const T*>(p.k);
-  const T* __restrict__ vg = static_cast<const T*>(p.v);
-  T* __restrict__ og = static_cast<T*>(p.o);
   constexpr int kWaves = kAttnThreads16 / 64;
   constexpr int kPerPass = kWaves * kQBlocksPerWave;
   const int nqb = (n + kQBlock - 1) / kQBlock;
@@ -266,21 +307,19 @@ __device__ __forceinline__ void attend_seq16(const AttnParams& p, int n, unsigne
   for (int pass = 0; pass < npass; ++pass) {
     int qb[2];
     bool act[2];
+    uint32_t qoff[2];
     V8 qf[2][2];
-    f32x4 o[2][4];
-    float m[2], l[2];
+    f32x4 o[2][5];
+    float m[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       qb[i] = pass * kPerPass + w + i * kWaves;
       act[i] = qb[i] < nqb;
       const int q = qb[i] * kQBlock + r16;
-      qf[i][0] = V8{};
-      qf[i][1] = V8{};
-      if (act[i] && q < n) {
-        const size_t e = elem(q);
-        qf[i][0] = *reinterpret_cast<const V8*>(qg + e + 8 * g);
-        qf[i][1] = *reinterpret_cast<const V8*>(qg + e + 32 + 8 * g);
-      }
+      qoff[i] = (act[i] && q < n) ? roff(q) : kOOB;
+      // B operand of S^T = K Q^T: lane (r16, g) holds Q[q][32 ks + 8 g .. + 7]
+      qf[i][0] = __builtin_bit_cast(V8, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)(qoff[i] + 16 * g), 0, 0));
+      qf[i][1] = __builtin_bit_cast(V8, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)(qoff[i] + 64 + 16 * g), 0, 0));
     }
     for (int cc = 0; cc < nchunk; ++cc) {
       // odd passes walk the chunks backwards so the chunk left staged by the
@@ -290,40 +329,38 @@ __device__ __forceinline__ void attend_seq16(const AttnParams& p, int n, unsigne
       const int rows = min(kc, n - c0);
       if (!(pass > 0 && cc == 0)) {
         if (pass > 0 || cc > 0) __syncthreads();
-        stage16<DT>(kg, vg, Ks, Vt, VP, c0, rows, elem);
+        stage16<DT>(rk, rv, Ks, Vt, VP, c0, rows, roff);
         __syncthreads();
       }
       if (cc == 0) {  // accumulators come alive only after the first staging
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
           m[i] = -INFINITY;
-          l[i] = 0.f;
 #pragma unroll
-          for (int db = 0; db < 4; ++db) o[i][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int db = 0; db < 5; ++db) o[i][db] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
       }
       if (act[0]) {
         const int ntile = (rows + kKeyTile - 1) / kKeyTile;
         for (int t = 0; t < ntile; ++t) {
           const int k0 = t * kKeyTile;
-          tile16<DT>(Ks, Vt, VP, k0, min(kKeyTile, rows - k0), qf, o, m, l, act[1], c);
+          tile16<DT>(Ks, Vt, VP, k0, min(kKeyTile, rows - k0), qf, o, m, act[1], c);
         }
       }
     }
+    // O^T block db, lane (r16, g) holds O[q][16 db + 4 g .. + 3]; o[i][4] holds
+    // the query's probability sum in every element.  Rows q >= n go to kOOB.
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       if (!act[i]) continue;
-      const float inv = 1.f / quad_sum(l[i]);
-      const int q = qb[i] * kQBlock + r16;
-      if (q < n) {
-        const size_t e = elem(q);
+      const float inv = 1.f / o[i][4][0];
 #pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          V4 out;
+      for (int db = 0; db < 4; ++db) {
+        V4 out;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) out[j] = (T)(o[i][db][j] * inv);
-          *reinterpret_cast<V4*>(og + e + db * 16 + 4 * g) = out;
-        }
+        for (int j = 0; j < 4; ++j) out[j] = (T)(o[i][db][j] * inv);
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, out), ro,
+                                              (int)(qoff[i] + db * 32 + 8 * g), 0, 0);
       }
     }
   }
@@ -389,7 +426,7 @@ __device__ __forceinline__ void stage32(const float* __restrict__ kg, const floa
     vr[u] = kr[u];
     const int r = e >> 4, pc = e & 15;
     if (e < total && r < rows) {
-      const size_t el = elem(c0 + r) + pc * 4;
+      const uint32_t el = elem(c0 + r) + pc * 4;
       kr[u] = *reinterpret_cast<const u32x4*>(kg + el);
       vr[u] = *reinterpret_cast<const u32x4*>(vg + el);
     }
@@ -441,7 +478,7 @@ __device__ __forceinline__ void attend_seq32(const AttnParams& p, int n, unsigne
 #pragma unroll
       for (int t4 = 0; t4 < 4; ++t4) qf[i][t4] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (act[i] && q < n) {
-        const size_t e = elem(q);
+        const uint32_t e = elem(q);
 #pragma unroll
         for (int t4 = 0; t4 < 4; ++t4) qf[i][t4] = *reinterpret_cast<const f32x4*>(qg + e + 16 * g + 4 * t4);
       }
@@ -468,7 +505,7 @@ __device__ __forceinline__ void attend_seq32(const AttnParams& p, int n, unsigne
       const float inv = 1.f / quad_sum(l[i]);
       const int q = qb[i] * kQBlock + r16;
       if (q < n) {
-        const size_t e = elem(q);
+        const uint32_t e = elem(q);
 #pragma unroll
         for (int db = 0; db < 4; ++db)
           *reinterpret_cast<f32x4*>(og + e + db * 16 + 4 * g) = o[i][db] * inv;
@@ -479,20 +516,31 @@ __device__ __forceinline__ void attend_seq32(const AttnParams& p, int n, unsigne
 
 // ---------------------------------------------------------------- kernels
 
-// Zero the output rows of pruned tokens of image b, head h (fused form).
+// Zero the output rows of pruned tokens of one (image, head); `o` points at
+// the head's slice of the image's first token row.
 template <int NT, int ESIZE>
-__device__ __forceinline__ void zero_pruned(void* o, const uint64_t* ballots, int b, int N, int H,
-                                            int h) {
+__device__ __forceinline__ void zero_pruned(char* o, const uint64_t* ballots, int N, int H) {
   constexpr int PIECES = kHeadDim * ESIZE / 16;
+  const uint32_t rs = (uint32_t)(H * kHeadDim * ESIZE);
   const int total = N * PIECES;
-  char* base = static_cast<char*>(o);
   for (int e = threadIdx.x; e < total; e += NT) {
     const int j = e / PIECES, pc = e - j * PIECES;
     const bool kept = (ballots[j >> 6] >> (j & 63)) & 1ull;
-    if (!kept)
-      *reinterpret_cast<u32x4*>(base + (((size_t)b * N + j) * H + h) * (kHeadDim * ESIZE) + pc * 16) =
-          u32x4{0u, 0u, 0u, 0u};
+    if (!kept) *reinterpret_cast<u32x4*>(o + (uint32_t)j * rs + pc * 16) = u32x4{0u, 0u, 0u, 0u};
   }
+}
+
+// The same parameters with q/k/v/o moved to one sequence's head slice, so
+// every per-row address inside is a 32-bit offset from a uniform base (an
+// image's rows span at most N * H * 64 * 4 bytes < 2^32).
+__device__ __forceinline__ AttnParams rebase(const AttnParams& p, size_t elem0, int esize) {
+  AttnParams r = p;
+  const size_t off = elem0 * (size_t)esize;
+  r.q = static_cast<const char*>(p.q) + off;
+  r.k = static_cast<const char*>(p.k) + off;
+  r.v = static_cast<const char*>(p.v) + off;
+  r.o = static_cast<char*>(p.o) + off;
+  return r;
 }
 
 template <int DT, bool FUSED>
@@ -510,29 +558,41 @@ __device__ __forceinline__ void attend_body(const AttnParams& p, unsigned char* 
   }
   const int b = bid / p.H, h = bid - b * p.H;
   const int H = p.H, N = p.N;
+  constexpr int ES = DT == 0 ? 4 : 2;
+  const uint32_t rs = (uint32_t)(H * kHeadDim);  // elements between consecutive token rows
   if constexpr (FUSED) {
     int32_t* idx = reinterpret_cast<int32_t*>(smem);
     const size_t off = (size_t)round_up(N * 4, 16);
     uint64_t* ballots = reinterpret_cast<uint64_t*>(smem + off);
     int32_t* cnt = reinterpret_cast<int32_t*>(smem + off + 16 * 8);
     const int n = compact_row<NT>(p.mask + (size_t)b * N, N, idx, nullptr, ballots, cnt);
-    zero_pruned<NT, DT == 0 ? 4 : 2>(p.o, ballots, b, N, H, h);
+    const AttnParams pl = rebase(p, ((size_t)b * N * H + h) * kHeadDim, ES);
+    zero_pruned<NT, ES>(static_cast<char*>(pl.o), ballots, N, H);
     if (n <= 0) return;
     unsigned char* kvbase = smem + attn_compact_bytes(N);
-    auto elem = [=](int r) -> size_t { return (((size_t)b * N + idx[r]) * H + h) * kHeadDim; };
-    if constexpr (DT == 0)
-      attend_seq32(p, n, kvbase, elem);
-    else
-      attend_seq16<DT>(p, n, kvbase, elem);
+    auto elem = [=](int r) -> uint32_t { return (uint32_t)idx[r] * rs; };
+    if constexpr (DT == 0) {
+      attend_seq32(pl, n, kvbase, elem);
+    } else {
+      const uint32_t bytes = (uint32_t)N * rs * ES;
+      auto roff = [=](int r) -> uint32_t { return (uint32_t)idx[min(r, n - 1)] * (rs * ES); };
+      attend_seq16<DT>(pl, n, kvbase, make_rsrc(pl.q, bytes), make_rsrc(pl.k, bytes),
+                       make_rsrc(pl.v, bytes), make_rsrc(pl.o, bytes), roff);
+    }
   } else {
     const int row0 = p.cu[b];
     const int n = p.cu[b + 1] - row0;
     if (n <= 0) return;
-    auto elem = [=](int r) -> size_t { return (((size_t)row0 + r) * H + h) * kHeadDim; };
-    if constexpr (DT == 0)
-      attend_seq32(p, n, smem, elem);
-    else
-      attend_seq16<DT>(p, n, smem, elem);
+    const AttnParams pl = rebase(p, ((size_t)row0 * H + h) * kHeadDim, ES);
+    auto elem = [=](int r) -> uint32_t { return (uint32_t)r * rs; };
+    if constexpr (DT == 0) {
+      attend_seq32(pl, n, smem, elem);
+    } else {
+      const uint32_t bytes = (uint32_t)n * rs * ES;
+      auto roff = [=](int r) -> uint32_t { return (uint32_t)r * (rs * ES); };
+      attend_seq16<DT>(pl, n, smem, make_rsrc(pl.q, bytes), make_rsrc(pl.k, bytes),
+                       make_rsrc(pl.v, bytes), make_rsrc(pl.o, bytes), roff);
+    }
   }
 }
 
