@@ -235,8 +235,9 @@ __device__ __forceinline__ void stage16(Rsrc rk, Rsrc rv, typename Half16<DT>::T
                                         typename Half16<DT>::T* Vt, int VP, int c0, int rows,
                                         RowOff roff) {
   constexpr int NT = kAttnThreads16;
-  constexpr int UK = kKcMax16 * 8 / NT;       // K pieces per thread at most
-  constexpr int UV = kKcMax16 / 4 * 16 / NT;  // V^T blocks per thread at most
+  constexpr int UK = (kKcMax16 * 8 + NT - 1) / NT;       // K pieces per thread at most
+  constexpr int UV = (kKcMax16 / 4 * 16 + NT - 1) / NT;  // V^T blocks per thread at most
+  static_assert(kKcMax16 % kKeyTile == 0, "chunks are whole key tiles");
   const int tid = threadIdx.x;
   const int rpad = round_up(rows, kKeyTile);
   const int kitems = rpad * 8, vitems = rpad / 4 * 16;

@@ -20,7 +20,7 @@ constexpr int kScanThreads = 1024;
 // Keys staged on chip per chunk.  16-bit: K rows [kc][64] halves (16-byte
 // pieces XOR-swizzled by row) + V^T [64][kc + 8] halves; fp32: K and V rows
 // [kc][68] floats.
-constexpr int kKcMax16 = 128;
+constexpr int kKcMax16 = 192;
 constexpr int kKcMax32 = 128;
 constexpr int kVPad16 = 8;     // halves of pad per staged V^T row
 constexpr int kPitch32 = 68;   // floats per staged K/V row for fp32
