@@ -17,6 +17,7 @@ kernel (direct and captured); and the fp64 CPU oracle timed on this host.
 """
 import argparse
 import hashlib
+import re
 import json
 import os
 import statistics
@@ -39,10 +40,16 @@ def log(*a):
 
 
 def kernel_source_hash():
+    """Hash of the attention kernel's code with comments and blank space
+    removed, so that counters taken on a kernel stay attached to it until
+    its code (not its commentary) changes."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p)) as f:
+            src = f.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 

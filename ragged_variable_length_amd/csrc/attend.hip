@@ -7,19 +7,18 @@
 // Work decomposition (CDNA4 / gfx950), 16-bit inputs:
 //  * one workgroup of 4 waves per (image, head).  Post-pruning ViT sequences
 //    are short (at most 197 tokens at 224x224, 577 at 384x384), so the
-//    workgroup stages its sequence's V once, transposed, in LDS; longer
-//    sequences are staged in chunks;
+//    workgroup stages its sequence's K and V (V transposed) in LDS in one
+//    memory round trip; sequences longer than one chunk are staged in chunks;
 //  * each wave owns two query blocks of 16 rows at a time and walks the keys
 //    32 at a time;
 //  * scores are formed transposed, S^T = K Q^T, with the 16x16x32 matrix-core
 //    product: each lane then holds one query and 4+4 keys, which is exactly
 //    the per-lane slice the second product O^T = V^T P^T takes as its B
-//    operand, so P never leaves registers.  The A operand of the first
-//    product is 16 contiguous bytes of a K row, so K goes straight from
-//    memory into registers (one tile ahead of use) and needs no LDS;
+//    operand, so P never leaves registers;
 //  * softmax in fp32 with exp2 (log2 e folded into the scale).  The running
 //    max is shared by the four lanes of a query with two lane-swap steps;
-//    row sums stay per lane until the end.  The output is rescaled only when
+//    row sums come from the matrix cores (an all-ones operand times the
+//    rounded probabilities).  The output is rescaled only when
 //    the max grows by more than 2^8 (the stale max still bounds every
 //    probability by 2^8, far inside fp16/bf16 range, and cancels exactly in
 //    the final division);
