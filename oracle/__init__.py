@@ -9,3 +9,4 @@ from .ragged import (  # noqa: F401
     seqlens,
     unpack,
 )
+from .threshold_l2 import keep_rank, sq_norms, threshold_l2_mask  # noqa: F401,E402

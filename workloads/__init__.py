@@ -153,7 +153,7 @@ def deit_s_224_threshold_l2(seed: int = 1002) -> Workload:
         mask[b, 1:] = (norms[b, 1:] >= thr).astype(np.uint8)
     q, k, v = [_cast((x @ w).astype(np.float32).reshape(B, N, H, d), "bf16") for w in ws]
     return Workload("deit_s_224_b4_h6_bf16_thresholdL2", B, N, H, d, "bf16", mask, q, k, v,
-                    {"seed": seed})
+                    {"seed": seed, "x": x.astype(np.float32), "keep_quantile": 0.5})
 
 
 DEIT_B_224_RATES = (0.0, 0.2, 0.5, 0.8)
@@ -206,6 +206,14 @@ def mixed_peak(seed: int = 1005, B: int = 1024) -> Workload:
     q, k, v = _normal_qkv(rng, B, N, H, HEAD_DIM, "f16")
     return Workload(f"mixed_b{B}_n197_h12_f16", B, N, H, HEAD_DIM, "f16", mask, q, k, v,
                     {"seed": seed})
+
+
+def embeddings(seed: int = 1006, B: int = 1024, N: int = 197, C: int = 768,
+               dtype: str = "f16") -> np.ndarray:
+    """Token embeddings x ~ N(0, 1) of shape [B, N, C] in the dtype's bit
+    container: the input of the Threshold-l2 keep-mask at DeiT-B width."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return _cast(rng.standard_normal((B, N, C), dtype=np.float32), dtype)
 
 
 def all_configs():
