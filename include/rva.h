@@ -55,6 +55,7 @@ extern "C" {
 #define RVA_MAX_TOKENS 1024
 #define RVA_MAX_HEADS 64
 #define RVA_HEAD_DIM 64
+#define RVA_MAX_CHANNELS 65536
 
 typedef enum { RVA_F32 = 0, RVA_F16 = 1, RVA_BF16 = 2 } rva_dtype;
 
@@ -126,12 +127,40 @@ int rva_fused(const void* q_pad, const void* k_pad, const void* v_pad, const uin
               void* o_pad, int32_t* cu_seqlens, int32_t* max_seqlen, void* stream);
 
 /*
+ * rva_threshold_l2_mask -- the Threshold-l2 keep-mask that feeds the path
+ * (one of the four pruning algorithms the aissential.tech summary lists in
+ * its "Summary"; the pages give no definition, the reading below is this
+ * library's).
+ *
+ * Per image: token 0 (CLS) is kept; patch token j (1 <= j < N) is kept when
+ * the L2 norm of its embedding row x[b, j, :] reaches the keep_quantile-th
+ * quantile (linear interpolation) of the image's N - 1 patch norms.  In
+ * exact arithmetic that keeps the patches whose norm is at least the r0-th
+ * smallest patch norm (0-based), r0 = ceil(keep_quantile * (N - 2)), which is
+ * the form evaluated: with distinct norms exactly N - 1 - r0 patches are
+ * kept; equal norms are kept or dropped together.  Decisions are taken on
+ * squared norms in fp64, summed in channel order c = 0..C-1 (each square is
+ * exact in fp64), so they are reproducible bit for bit.
+ *   x        : [B, N, C] row-major embeddings in `dtype` (16-byte aligned);
+ *              C * element size must be a multiple of 16 bytes,
+ *              1 <= C <= RVA_MAX_CHANNELS.
+ *   keep_quantile : in [0, 1]; 0 keeps every patch, 1 only the largest.
+ *   mask_out : uint8 [B, N] output (1 = keep, 0 = prune).
+ * One kernel launch of B workgroups.
+ */
+int rva_threshold_l2_mask(const void* x, int B, int N, int C, int dtype, double keep_quantile,
+                          uint8_t* mask_out, void* stream);
+
+/*
  * Launch plans -- capture once, replay with one graph launch per call (the
  * Abstract's per-call dispatch floor is what this removes).
  *
  * mode RVA_PLAN_STAGED : rva_pack, rva_ragged_attend, rva_unpack (4 kernels).
  *      RVA_PLAN_FUSED  : rva_fused (1 kernel).
  *      RVA_PLAN_EMPTY  : one empty one-workgroup kernel (measures the floor).
+ *      RVA_PLAN_L2_FUSED : rva_threshold_l2_mask from x into mask_out, then
+ *                        rva_fused reading mask_out (2 kernels); `mask` is
+ *                        ignored.
  * Every pointer and size is fixed at creation; the CONTENTS of the inputs
  * (including the mask) may change between launches.  Staged mode needs the
  * packed scratch buffers q/k/v/o_packed (capacity B*N rows each) and
@@ -141,7 +170,12 @@ int rva_fused(const void* q_pad, const void* k_pad, const void* v_pad, const uin
  * stream and instantiates a HIP graph (host-side allocation by the runtime);
  * rva_plan_launch enqueues one graph launch on `stream`.
  */
-typedef enum { RVA_PLAN_STAGED = 0, RVA_PLAN_FUSED = 1, RVA_PLAN_EMPTY = 2 } rva_plan_mode;
+typedef enum {
+  RVA_PLAN_STAGED = 0,
+  RVA_PLAN_FUSED = 1,
+  RVA_PLAN_EMPTY = 2,
+  RVA_PLAN_L2_FUSED = 3
+} rva_plan_mode;
 
 typedef struct {
   int mode;
@@ -160,6 +194,12 @@ typedef struct {
   int32_t* max_seqlen;
   int32_t* kept_index;
   void* o_pad;
+  /* keep-mask stage (RVA_PLAN_L2_FUSED): as rva_threshold_l2_mask */
+  const void* x;
+  int C;
+  int x_dtype;
+  double keep_quantile;
+  uint8_t* mask_out;
 } rva_plan_desc;
 
 typedef struct rva_plan_s* rva_plan;

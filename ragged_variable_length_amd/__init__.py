@@ -15,14 +15,15 @@ import os
 
 import torch
 
-__all__ = ["RVAError", "lib", "pack", "ragged_attend", "unpack", "fused", "Plan", "empty",
-           "dtype_code", "F32", "F16", "BF16", "STAGED", "FUSED", "EMPTY", "MAX_TOKENS"]
+__all__ = ["RVAError", "lib", "pack", "ragged_attend", "unpack", "fused", "threshold_l2_mask",
+           "Plan", "empty", "dtype_code", "F32", "F16", "BF16", "STAGED", "FUSED", "EMPTY",
+           "L2_FUSED", "MAX_TOKENS"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "librva.so")
 
 F32, F16, BF16 = 0, 1, 2
-STAGED, FUSED, EMPTY = 0, 1, 2
+STAGED, FUSED, EMPTY, L2_FUSED = 0, 1, 2, 3
 MAX_TOKENS = 1024
 HEAD_DIM = 64
 
@@ -44,7 +45,9 @@ class _PlanDesc(ctypes.Structure):
                 ("k_packed", ctypes.c_void_p), ("v_packed", ctypes.c_void_p),
                 ("o_packed", ctypes.c_void_p), ("cu_seqlens", ctypes.c_void_p),
                 ("max_seqlen", ctypes.c_void_p), ("kept_index", ctypes.c_void_p),
-                ("o_pad", ctypes.c_void_p)]
+                ("o_pad", ctypes.c_void_p), ("x", ctypes.c_void_p), ("C", ctypes.c_int),
+                ("x_dtype", ctypes.c_int), ("keep_quantile", ctypes.c_double),
+                ("mask_out", ctypes.c_void_p)]
 
 
 _lib = None
@@ -68,13 +71,15 @@ def lib() -> ctypes.CDLL:
     L.rva_plan_launch.argtypes = [P, P]
     L.rva_plan_destroy.argtypes = [P]
     L.rva_empty.argtypes = [I, P]
+    L.rva_threshold_l2_mask.argtypes = [P, I, I, I, I, ctypes.c_double, P, P]
     L.rva_status_string.argtypes = [I]
     L.rva_status_string.restype = ctypes.c_char_p
     L.rva_last_error.argtypes = []
     L.rva_last_error.restype = ctypes.c_char_p
     L.rva_version.argtypes = []
     for name in ("rva_pack", "rva_ragged_attend", "rva_unpack", "rva_fused", "rva_plan_create",
-                 "rva_plan_launch", "rva_plan_destroy", "rva_empty", "rva_version"):
+                 "rva_plan_launch", "rva_plan_destroy", "rva_empty", "rva_version",
+                 "rva_threshold_l2_mask"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -197,6 +202,19 @@ def fused(q, k, v, mask, *, max_seqlen_hint: int = 0, scale: float | None = None
     return out
 
 
+def threshold_l2_mask(x, keep_quantile: float, *, out=None, stream=None):
+    """Threshold-l2 keep-mask of embeddings x [B,N,C]: uint8 [B,N], CLS kept,
+    patch kept when its L2 norm reaches the per-image keep_quantile of the
+    patch norms."""
+    _req(x, "x")
+    B, N, C = x.shape
+    if out is None:
+        out = torch.empty((B, N), dtype=torch.uint8, device=x.device)
+    _check(lib().rva_threshold_l2_mask(_ptr(x), B, N, C, dtype_code(x), float(keep_quantile),
+                                       _ptr(out), _stream(stream)), "rva_threshold_l2_mask")
+    return out
+
+
 def empty(count: int = 1, stream=None):
     """Enqueue `count` empty one-workgroup kernels (dispatch-floor probe)."""
     _check(lib().rva_empty(int(count), _stream(stream)), "rva_empty")
@@ -211,8 +229,10 @@ class Plan:
 
     def __init__(self, mode: int, *, q=None, k=None, v=None, mask=None, out=None, scale=None,
                  max_seqlen_hint: int = 0, packed=None, cu_seqlens=None, max_seqlen=None,
-                 kept_index=None):
-        self._keep = [q, k, v, mask, out, packed, cu_seqlens, max_seqlen, kept_index]
+                 kept_index=None, x=None, keep_quantile: float = 0.5):
+        """mode L2_FUSED: the keep-mask of `x` is written into `mask` by the
+        plan, then read by the fused attention."""
+        self._keep = [q, k, v, mask, out, packed, cu_seqlens, max_seqlen, kept_index, x]
         desc = _PlanDesc()
         desc.mode = mode
         desc.d = HEAD_DIM
@@ -233,6 +253,14 @@ class Plan:
             desc.cu_seqlens = cu_seqlens.data_ptr() if cu_seqlens is not None else None
             desc.max_seqlen = max_seqlen.data_ptr() if max_seqlen is not None else None
             desc.kept_index = kept_index.data_ptr() if kept_index is not None else None
+            if mode == L2_FUSED:
+                _req(x, "x")
+                desc.x = x.data_ptr()
+                desc.C = x.shape[2]
+                desc.x_dtype = dtype_code(x)
+                desc.keep_quantile = float(keep_quantile)
+                desc.mask_out = desc.mask
+                desc.mask = None
         h = ctypes.c_void_p()
         _check(lib().rva_plan_create(ctypes.byref(desc), ctypes.byref(h)), "rva_plan_create")
         self._h = h

@@ -209,17 +209,9 @@ __device__ __forceinline__ void tile16(const typename Half16<DT>::T* __restrict_
   }
 }
 
-// Global accesses of the 16-bit path go through raw buffer descriptors whose
-// base is the sequence's head slice and whose size covers exactly its rows:
-// offsets are 32-bit, and an offset past the end (kOOB) reads zeros and
-// drops stores in hardware, so ragged tails need no branches.
-typedef __amdgpu_buffer_rsrc_t Rsrc;
-constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format (gfx9 family)
-constexpr uint32_t kOOB = 0x80000000u;   // beyond any descriptor size used here
-
-__device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRsrcWord3);
-}
+// Global accesses of the 16-bit path go through raw buffer descriptors
+// (make_rsrc) whose base is the sequence's head slice and whose size covers
+// exactly its rows, so ragged tails need no branches.
 
 // Stage keys [c0, c0 + rows) of the sequence: K rows into Ks (swizzled
 // 16-byte pieces), V transposed into Vt[d][key].  Every load of the chunk is

@@ -68,8 +68,11 @@ std::once_flag g_init_once;
 hipError_t g_init_err = hipSuccess;
 
 int ensure_init() {
-  std::call_once(g_init_once, [] { g_init_err = rva::attend_init(); });
-  if (g_init_err != hipSuccess) return hip_fail(g_init_err, "attention kernel set-up");
+  std::call_once(g_init_once, [] {
+    g_init_err = rva::attend_init();
+    if (g_init_err == hipSuccess) g_init_err = rva::threshold_init();
+  });
+  if (g_init_err != hipSuccess) return hip_fail(g_init_err, "kernel set-up");
   return RVA_OK;
 }
 
@@ -218,6 +221,46 @@ int validate_fused(const void* q, const void* k, const void* v, const uint8_t* m
   return RVA_OK;
 }
 
+struct ThreshArgs {
+  rva::ThreshParams p;
+  int B;
+  int dtype;
+};
+
+int validate_threshold(const void* x, int B, int N, int C, int dtype, double keep_quantile,
+                       uint8_t* mask_out, ThreshArgs* out) {
+  if (dtype != RVA_F32 && dtype != RVA_F16 && dtype != RVA_BF16)
+    return fail(RVA_ERR_INVALID, "unknown dtype %d", dtype);
+  if (B < 1) return fail(RVA_ERR_INVALID, "B must be >= 1 (got %d)", B);
+  if (N < 1 || N > RVA_MAX_TOKENS)
+    return fail(RVA_ERR_INVALID, "N must be in [1, %d] (got %d)", RVA_MAX_TOKENS, N);
+  if ((long long)B * N >= (1ll << 31)) return fail(RVA_ERR_INVALID, "B*N must be < 2^31");
+  if (C < 1 || C > RVA_MAX_CHANNELS)
+    return fail(RVA_ERR_INVALID, "C must be in [1, %d] (got %d)", RVA_MAX_CHANNELS, C);
+  if ((C * esize(dtype)) % 16 != 0)
+    return fail(RVA_ERR_INVALID, "C * element size must be a multiple of 16 bytes (C = %d)", C);
+  if (!(keep_quantile >= 0.0 && keep_quantile <= 1.0))
+    return fail(RVA_ERR_INVALID, "keep_quantile must lie in [0, 1]");
+  RVA_TRY(check_data(x, "x", true));
+  if (!mask_out) return fail(RVA_ERR_INVALID, "mask_out is NULL");
+  const int P = N - 1;
+  out->p.x = x;
+  out->p.mask = mask_out;
+  out->p.N = N;
+  out->p.C = C;
+  out->p.r0 = P >= 1 ? (int)ceil(keep_quantile * (double)(P - 1)) : 0;
+  out->B = B;
+  out->dtype = dtype;
+  return RVA_OK;
+}
+
+int enqueue_threshold(const ThreshArgs& a, hipStream_t s) {
+  RVA_TRY(ensure_init());
+  hipError_t e = rva::launch_threshold(a.p, a.B, a.dtype, s);
+  if (e != hipSuccess) return hip_fail(e, "keep-mask launch");
+  return RVA_OK;
+}
+
 int enqueue_attend(const rva::AttnParams& p, int dtype, bool fused, hipStream_t s) {
   RVA_TRY(ensure_init());
   hipError_t e = rva::launch_attend(p, dtype, fused, s);
@@ -234,7 +277,7 @@ struct rva_plan_s {
 
 extern "C" {
 
-int rva_version(void) { return 100; }
+int rva_version(void) { return 101; }
 
 const char* rva_status_string(int status) {
   switch (status) {
@@ -283,6 +326,13 @@ int rva_fused(const void* q_pad, const void* k_pad, const void* v_pad, const uin
   return enqueue_attend(p, dtype, true, static_cast<hipStream_t>(stream));
 }
 
+int rva_threshold_l2_mask(const void* x, int B, int N, int C, int dtype, double keep_quantile,
+                          uint8_t* mask_out, void* stream) {
+  ThreshArgs a;
+  RVA_TRY(validate_threshold(x, B, N, C, dtype, keep_quantile, mask_out, &a));
+  return enqueue_threshold(a, static_cast<hipStream_t>(stream));
+}
+
 int rva_empty(int count, void* stream) {
   if (count < 0) return fail(RVA_ERR_INVALID, "count must be >= 0");
   for (int i = 0; i < count; ++i) {
@@ -298,6 +348,7 @@ int rva_plan_create(const rva_plan_desc* desc, rva_plan* out) {
   const rva_plan_desc& D = *desc;
   PackArgs pack, unpack;
   rva::AttnParams attn;
+  ThreshArgs thr;
   switch (D.mode) {
     case RVA_PLAN_STAGED:
       RVA_TRY(validate_pack(D.q_pad, D.k_pad, D.v_pad, D.mask, D.B, D.N, D.H, D.d, D.dtype,
@@ -313,6 +364,13 @@ int rva_plan_create(const rva_plan_desc* desc, rva_plan* out) {
       break;
     case RVA_PLAN_FUSED:
       RVA_TRY(validate_fused(D.q_pad, D.k_pad, D.v_pad, D.mask, D.B, D.N, D.H, D.d,
+                             D.max_seqlen_hint, D.softmax_scale, D.dtype, D.o_pad, D.cu_seqlens,
+                             D.max_seqlen, &attn));
+      break;
+    case RVA_PLAN_L2_FUSED:
+      RVA_TRY(validate_threshold(D.x, D.B, D.N, D.C, D.x_dtype, D.keep_quantile, D.mask_out,
+                                 &thr));
+      RVA_TRY(validate_fused(D.q_pad, D.k_pad, D.v_pad, D.mask_out, D.B, D.N, D.H, D.d,
                              D.max_seqlen_hint, D.softmax_scale, D.dtype, D.o_pad, D.cu_seqlens,
                              D.max_seqlen, &attn));
       break;
@@ -343,6 +401,10 @@ int rva_plan_create(const rva_plan_desc* desc, rva_plan* out) {
       break;
     case RVA_PLAN_FUSED:
       st = enqueue_attend(attn, D.dtype, true, cs);
+      break;
+    case RVA_PLAN_L2_FUSED:
+      st = enqueue_threshold(thr, cs);
+      if (st == RVA_OK) st = enqueue_attend(attn, D.dtype, true, cs);
       break;
     case RVA_PLAN_EMPTY:
       e = rva::launch_empty(cs);

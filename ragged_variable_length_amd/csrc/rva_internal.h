@@ -49,6 +49,13 @@ struct CopyParams {
   int row_bytes;          // H * d * element size (multiple of 16)
 };
 
+struct ThreshParams {
+  const void* x;          // token embeddings [B, N, C]
+  uint8_t* mask;          // keep-mask output [B, N]
+  int N, C;
+  int r0;                 // 0-based order statistic a kept patch's norm must reach
+};
+
 __host__ __device__ inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
 
 inline int attn_kc_max(int dtype) { return dtype == 0 ? kKcMax32 : kKcMax16; }
@@ -78,5 +85,7 @@ hipError_t launch_unpack(const CopyParams& p, int splits, hipStream_t s);
 hipError_t launch_attend(const AttnParams& p, int dtype, bool fused, hipStream_t s);
 hipError_t launch_empty(hipStream_t s);
 hipError_t attend_init();  // raises the dynamic-LDS limit of every attention kernel
+hipError_t launch_threshold(const ThreshParams& p, int B, int dtype, hipStream_t s);
+hipError_t threshold_init();  // raises the dynamic-LDS limit of the keep-mask kernels
 
 }  // namespace rva

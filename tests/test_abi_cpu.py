@@ -14,7 +14,7 @@ HEADER = os.path.join(ROOT, "include", "rva.h")
 def _declared():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(rva_[a-z_]+)\s*\(",
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(rva_[a-z0-9_]+)\s*\(",
                        src, flags=re.M)
     return sorted(set(names))
 
@@ -32,7 +32,7 @@ def test_header_lists_the_entry_points():
     names = _declared()
     for want in ("rva_pack", "rva_ragged_attend", "rva_unpack", "rva_fused", "rva_plan_create",
                  "rva_plan_launch", "rva_plan_destroy", "rva_empty", "rva_status_string",
-                 "rva_last_error", "rva_version"):
+                 "rva_last_error", "rva_version", "rva_threshold_l2_mask"):
         assert want in names
 
 
@@ -47,7 +47,7 @@ def test_status_strings(L):
     assert L.rva_status_string(-2) == b"unsupported configuration"
     assert L.rva_status_string(-3) == b"HIP runtime error"
     assert L.rva_status_string(99) == b"unknown status"
-    assert L.rva_version() == 100
+    assert L.rva_version() == 101
 
 
 FAKE = ctypes.c_void_p(0x7F0000000000)  # aligned, never dereferenced: validation fails first
@@ -85,6 +85,22 @@ def test_attend_unpack_fused_validation(L):
     assert L.rva_empty(-1, None) == -1
 
 
+def test_threshold_validation(L):
+    def thr(x=FAKE, B=2, N=197, C=384, dt=0, q=0.5, m=FAKE):
+        return L.rva_threshold_l2_mask(x, B, N, C, dt, ctypes.c_double(q), m, None)
+    assert thr(x=None) == -1 and b"x is NULL" in L.rva_last_error()
+    assert thr(m=None) == -1 and b"mask_out" in L.rva_last_error()
+    assert thr(x=MIS) == -1 and b"aligned" in L.rva_last_error()
+    assert thr(B=0) == -1 and thr(N=0) == -1 and thr(N=1025) == -1
+    assert thr(C=0) == -1 and thr(C=65537) == -1
+    assert thr(C=6, dt=0) == -1 and b"16 bytes" in L.rva_last_error()
+    assert thr(C=12, dt=1) == -1 and thr(C=12, dt=2) == -1
+    assert thr(dt=5) == -1 and b"dtype" in L.rva_last_error()
+    assert thr(q=-0.1) == -1 and thr(q=1.5) == -1 and thr(q=float("nan")) == -1
+    assert b"keep_quantile" in L.rva_last_error()
+    assert thr(B=1 << 22, N=1024) == -1
+
+
 def test_plan_validation(L):
     import ragged_variable_length_amd as rva
     d = rva._PlanDesc()
@@ -96,6 +112,15 @@ def test_plan_validation(L):
     d.B, d.N, d.H, d.d, d.dtype = 2, 8, 1, 64, 1
     assert L.rva_plan_create(ctypes.byref(d), ctypes.byref(h)) == -1  # null pointers
     assert h.value is None
+    d.mode = rva.L2_FUSED
+    d.q_pad = d.k_pad = d.v_pad = d.o_pad = 0x7F0000000000
+    d.mask = None
+    d.x, d.C, d.x_dtype, d.keep_quantile, d.mask_out = 0x7F0000000000, 384, 0, 2.0, 0x7F0000000000
+    assert L.rva_plan_create(ctypes.byref(d), ctypes.byref(h)) == -1  # keep_quantile range
+    assert b"keep_quantile" in L.rva_last_error()
+    d.keep_quantile, d.mask_out = 0.5, None
+    assert L.rva_plan_create(ctypes.byref(d), ctypes.byref(h)) == -1
+    assert b"mask_out" in L.rva_last_error()
     assert L.rva_plan_launch(None, None) == -1
     assert L.rva_plan_destroy(None) == 0
 
