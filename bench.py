@@ -230,6 +230,43 @@ def measure_config(ctx, w, reps, floor_us):
     return res
 
 
+def measure_threshold(ctx, reps):
+    """The Threshold-l2 keep-mask: alone on DeiT-B-width embeddings for 1024
+    images, and in front of the fused path on the DeiT-S recipe (direct
+    calls and the captured two-kernel plan)."""
+    import workloads as W
+    t, rva = ctx.torch, ctx.rva
+    x = W.embeddings()
+    B, N, C = x.shape
+    xd = t.from_numpy(x).to(ctx.dev)
+    mask = t.empty((B, N), dtype=t.uint8, device=ctx.dev)
+    fn = lambda: rva.threshold_l2_mask(xd, 0.5, out=mask)
+    for _ in range(3):
+        fn()
+    cold = ctx.cold_time(fn, max(5, reps // 10))
+    warm = ctx.events_time(fn, reps)
+    nbytes = B * N * C * x.itemsize + B * N
+    res = {"embeddings": {"B": B, "N": N, "C": C, "dtype": "f16", "keep_quantile": 0.5,
+                          "kernel_us_cold": round(cold, 2), "kernel_us_warm": round(warm, 2),
+                          "bytes": nbytes, "GBps_cold": round(nbytes / (cold * 1e-6) / 1e9, 1),
+                          "frac_hbm_cold": round(nbytes / (cold * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}}
+    del xd, mask
+    w = W.deit_s_224_threshold_l2()
+    q, k, v, _ = upload(ctx, w)
+    xs = t.from_numpy(w.meta["x"]).to(ctx.dev)
+    m = t.empty((w.B, w.N), dtype=t.uint8, device=ctx.dev)
+    out = t.empty_like(q)
+
+    def direct():
+        rva.threshold_l2_mask(xs, 0.5, out=m)
+        rva.fused(q, k, v, m, out=out)
+    plan = rva.Plan(rva.L2_FUSED, q=q, k=k, v=v, mask=m, out=out, x=xs, keep_quantile=0.5)
+    res["deit_s_mask_then_fused"] = {"direct": timings(ctx, direct, reps),
+                                     "plan": timings(ctx, plan.launch, reps)}
+    plan.close()
+    return res
+
+
 def measure_floor(ctx, reps):
     rva = ctx.rva
     plan = rva.Plan(rva.EMPTY)
@@ -472,6 +509,8 @@ def main():
                                       floor["graph_latency_us"]))
             torch.cuda.empty_cache()
         line["per_config"] = per
+        log("measuring the keep-mask ...")
+        line["threshold_l2"] = measure_threshold(ctx, reps)
     if not args.no_cpu:
         log("timing the CPU oracle ...")
         line["cpu_baseline"] = cpu_baseline(w)
