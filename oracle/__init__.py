@@ -10,3 +10,4 @@ from .ragged import (  # noqa: F401
     unpack,
 )
 from .threshold_l2 import keep_rank, sq_norms, threshold_l2_mask  # noqa: F401,E402
+from .projection import linear, out_projection, qkv_projection  # noqa: F401,E402

@@ -216,6 +216,20 @@ def embeddings(seed: int = 1006, B: int = 1024, N: int = 197, C: int = 768,
     return _cast(rng.standard_normal((B, N, C), dtype=np.float32), dtype)
 
 
+def projection_weights(seed: int = 1007, C: int = 768, dtype: str = "f16") -> dict:
+    """Synthetic attention-block weights in nn.Linear layout: W_qkv [3C, C] and
+    W_o [C, C] ~ N(0, 1/C) (variance), biases ~ N(0, 0.02^2), in the dtype's
+    bit container."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    s = np.float32(1.0 / np.sqrt(C))
+    w_qkv = rng.standard_normal((3 * C, C), dtype=np.float32) * s
+    b_qkv = rng.standard_normal(3 * C, dtype=np.float32) * np.float32(0.02)
+    w_o = rng.standard_normal((C, C), dtype=np.float32) * s
+    b_o = rng.standard_normal(C, dtype=np.float32) * np.float32(0.02)
+    return {k: _cast(v, dtype) for k, v in
+            (("w_qkv", w_qkv), ("b_qkv", b_qkv), ("w_o", w_o), ("b_o", b_o))}
+
+
 def all_configs():
     """The five workloads in order; the DeiT-B 224 sweep contributes one per rate."""
     yield tiny()
