@@ -152,6 +152,48 @@ int rva_threshold_l2_mask(const void* x, int B, int N, int C, int dtype, double 
                           uint8_t* mask_out, void* stream);
 
 /*
+ * Projections on the packed rows -- the two dense products of a ViT attention
+ * block, run on the T kept rows only.  The aissential.tech summary's
+ * "Method" has the packer feed the whole block, and its "In practice" asks
+ * for attention and the rest of the block to be timed apart; the pages give
+ * no formula, so these are the standard block's affine maps (nn.Linear
+ * layout: weight [out, in], y = x W^T + b).  fp16 and bf16 only (fp32
+ * returns RVA_ERR_UNSUPPORTED); 16-bit matrix-core products with fp32
+ * accumulation, bias and residual added in fp32, one rounding to the dtype.
+ * C = H * 64 with 1 <= H <= RVA_MAX_HEADS; B*N*C*2 < 2^31.  T is read on the
+ * device from cu_seqlens[B]: no host synchronisation, and every buffer
+ * indexed by packed row has a capacity of B*N rows.
+ *
+ * rva_qkv_projection: [q | k | v] = x_r W_qkv^T + b_qkv for packed rows r.
+ *   x          : with kept_index, padded embeddings [B, N, C] and row r is
+ *                x[kept_index[r]] (the pack's gather, fused); with
+ *                kept_index NULL, packed rows [T, C].
+ *   w_qkv      : [3C, C]; b_qkv: [3C] or NULL.
+ *   q, k, v    : packed outputs [T, C] = [T, H, 64] each (weight rows
+ *                0..C-1, C..2C-1 and 2C..3C-1).
+ * One kernel launch.
+ */
+int rva_qkv_projection(const void* x, const int32_t* kept_index, const int32_t* cu_seqlens,
+                       int B, int N, int C, const void* w_qkv, const void* b_qkv, int dtype,
+                       void* q, void* k, void* v, void* stream);
+
+/*
+ * rva_out_projection: y_r = o_r W_o^T + b_o (+ residual) for packed rows r.
+ *   o          : packed [T, C] (the attention output).
+ *   w_o        : [C, C]; b_o: [C] or NULL.
+ *   kept_index : with it, y and residual are padded [B, N, C]: row r goes to
+ *                y[kept_index[r]] and every row whose mask byte is 0 is
+ *                written as +0 (the unpack, fused; mask required); without
+ *                it, y and residual are packed [T, C].
+ *   residual   : added before rounding, or NULL.  It may be the same buffer
+ *                as y (in-place residual update).
+ * One kernel launch.
+ */
+int rva_out_projection(const void* o, const int32_t* kept_index, const int32_t* cu_seqlens,
+                       const uint8_t* mask, int B, int N, int C, const void* w_o,
+                       const void* b_o, const void* residual, int dtype, void* y, void* stream);
+
+/*
  * Launch plans -- capture once, replay with one graph launch per call (the
  * Abstract's per-call dispatch floor is what this removes).
  *

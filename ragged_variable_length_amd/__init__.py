@@ -16,6 +16,7 @@ import os
 import torch
 
 __all__ = ["RVAError", "lib", "pack", "ragged_attend", "unpack", "fused", "threshold_l2_mask",
+           "qkv_projection", "out_projection", "index",
            "Plan", "empty", "dtype_code", "F32", "F16", "BF16", "STAGED", "FUSED", "EMPTY",
            "L2_FUSED", "MAX_TOKENS"]
 
@@ -72,6 +73,8 @@ def lib() -> ctypes.CDLL:
     L.rva_plan_destroy.argtypes = [P]
     L.rva_empty.argtypes = [I, P]
     L.rva_threshold_l2_mask.argtypes = [P, I, I, I, I, ctypes.c_double, P, P]
+    L.rva_qkv_projection.argtypes = [P, P, P, I, I, I, P, P, I, P, P, P, P]
+    L.rva_out_projection.argtypes = [P, P, P, P, I, I, I, P, P, P, I, P, P]
     L.rva_status_string.argtypes = [I]
     L.rva_status_string.restype = ctypes.c_char_p
     L.rva_last_error.argtypes = []
@@ -79,7 +82,7 @@ def lib() -> ctypes.CDLL:
     L.rva_version.argtypes = []
     for name in ("rva_pack", "rva_ragged_attend", "rva_unpack", "rva_fused", "rva_plan_create",
                  "rva_plan_launch", "rva_plan_destroy", "rva_empty", "rva_version",
-                 "rva_threshold_l2_mask"):
+                 "rva_threshold_l2_mask", "rva_qkv_projection", "rva_out_projection"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -160,6 +163,23 @@ def pack(q, k, v, mask, *, outputs=None, kept_index=True, stream=None):
     return out
 
 
+def index(mask, *, out=None, stream=None):
+    """Offsets and kept-index list only (rva_pack with no row copies):
+    returns dict with cu_seqlens [B+1], max_seqlen [1], kept_index [B*N]
+    (capacity; entries past T unused)."""
+    m = _mask_u8(mask)
+    B, N = m.shape
+    out = dict(out or {})
+    dev = m.device
+    out.setdefault("cu_seqlens", torch.empty(B + 1, dtype=torch.int32, device=dev))
+    out.setdefault("max_seqlen", torch.empty(1, dtype=torch.int32, device=dev))
+    out.setdefault("kept_index", torch.empty(B * N, dtype=torch.int32, device=dev))
+    _check(lib().rva_pack(None, None, None, _ptr(m), B, N, 1, HEAD_DIM, F16, None, None, None,
+                          _ptr(out["cu_seqlens"]), _ptr(out["max_seqlen"]),
+                          _ptr(out["kept_index"]), _stream(stream)), "rva_pack")
+    return out
+
+
 def ragged_attend(q, k, v, cu_seqlens, max_seqlen: int, *, scale: float | None = None, out=None,
                   stream=None):
     """Attention over packed [T,H,64] q/k/v with offsets cu_seqlens [B+1]."""
@@ -212,6 +232,53 @@ def threshold_l2_mask(x, keep_quantile: float, *, out=None, stream=None):
         out = torch.empty((B, N), dtype=torch.uint8, device=x.device)
     _check(lib().rva_threshold_l2_mask(_ptr(x), B, N, C, dtype_code(x), float(keep_quantile),
                                        _ptr(out), _stream(stream)), "rva_threshold_l2_mask")
+    return out
+
+
+def qkv_projection(x, cu_seqlens, w_qkv, b_qkv=None, *, kept_index=None, B=None, N=None,
+                   out=None, stream=None):
+    """[q | k | v] = x_r W_qkv^T + b_qkv on the packed rows r.
+
+    x: padded [B,N,C] with kept_index (rows gathered), or packed [>=T, C]
+    without (then B and N give the capacity B*N).  Returns packed q, k, v of
+    capacity B*N rows, [B*N, C] each (rows past T = cu_seqlens[B] untouched).
+    """
+    _req(x, "x")
+    C = x.shape[-1]
+    if kept_index is not None:
+        B, N = x.shape[0], x.shape[1]
+    if B is None or N is None:
+        raise ValueError("packed input needs B and N")
+    if out is None:
+        out = tuple(torch.empty((B * N, C), dtype=x.dtype, device=x.device) for _ in range(3))
+    q, k, v = out
+    _check(lib().rva_qkv_projection(_ptr(x), _ptr(kept_index), _ptr(cu_seqlens), B, N, C,
+                                    _ptr(w_qkv), _ptr(b_qkv), dtype_code(x), _ptr(q), _ptr(k),
+                                    _ptr(v), _stream(stream)), "rva_qkv_projection")
+    return q, k, v
+
+
+def out_projection(o, cu_seqlens, w_o, b_o=None, *, kept_index=None, mask=None, B=None, N=None,
+                   residual=None, out=None, stream=None):
+    """y_r = o_r W_o^T + b_o (+ residual) on the packed rows r of o [>=T, C].
+
+    With kept_index and mask: y is padded [B,N,C], pruned rows +0, residual
+    padded.  Without: y packed [B*N, C] (capacity), residual packed.
+    """
+    _req(o, "o")
+    C = o.shape[-1]
+    m = None
+    if kept_index is not None:
+        m = _mask_u8(mask)
+        B, N = m.shape
+    if B is None or N is None:
+        raise ValueError("B and N are needed")
+    if out is None:
+        shape = (B, N, C) if kept_index is not None else (B * N, C)
+        out = torch.empty(shape, dtype=o.dtype, device=o.device)
+    _check(lib().rva_out_projection(_ptr(o), _ptr(kept_index), _ptr(cu_seqlens), _ptr(m), B, N, C,
+                                    _ptr(w_o), _ptr(b_o), _ptr(residual), dtype_code(o), _ptr(out),
+                                    _stream(stream)), "rva_out_projection")
     return out
 
 

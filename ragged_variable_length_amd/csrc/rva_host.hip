@@ -261,6 +261,99 @@ int enqueue_threshold(const ThreshArgs& a, hipStream_t s) {
   return RVA_OK;
 }
 
+// ---- projections
+
+int check_proj_shape(int B, int N, int C, int dtype) {
+  if (dtype != RVA_F16 && dtype != RVA_BF16)
+    return dtype == RVA_F32 ? fail(RVA_ERR_UNSUPPORTED, "projections take fp16 or bf16")
+                            : fail(RVA_ERR_INVALID, "unknown dtype %d", dtype);
+  if (B < 1) return fail(RVA_ERR_INVALID, "B must be >= 1 (got %d)", B);
+  if (N < 1 || N > RVA_MAX_TOKENS)
+    return fail(RVA_ERR_INVALID, "N must be in [1, %d] (got %d)", RVA_MAX_TOKENS, N);
+  if (C < RVA_HEAD_DIM || C > RVA_MAX_HEADS * RVA_HEAD_DIM || C % RVA_HEAD_DIM != 0)
+    return fail(RVA_ERR_INVALID, "C must be a multiple of 64 in [64, %d] (got %d)",
+                RVA_MAX_HEADS * RVA_HEAD_DIM, C);
+  // every row byte offset of the padded or packed buffers fits 31 bits
+  if ((long long)B * N * C * 2 >= (1ll << 31))
+    return fail(RVA_ERR_INVALID, "B*N*C*2 must be < 2^31");
+  return RVA_OK;
+}
+
+void linear_grid(rva::LinearParams* p) {
+  const int t = rva::linear_tile_size();
+  p->m_tiles = (p->M + t - 1) / t;
+  p->n_tiles = (p->Nout + t - 1) / t;
+}
+
+int validate_qkv(const void* x, const int32_t* kept_index, const int32_t* cu, int B, int N, int C,
+                 const void* w, const void* b, int dtype, void* q, void* k, void* v,
+                 rva::LinearParams* p) {
+  RVA_TRY(check_proj_shape(B, N, C, dtype));
+  RVA_TRY(check_data(x, "x", true));
+  RVA_TRY(check_i32(kept_index, "kept_index", false));
+  RVA_TRY(check_i32(cu, "cu_seqlens", true));
+  RVA_TRY(check_data(w, "w_qkv", true));
+  RVA_TRY(check_data(b, "b_qkv", false));
+  RVA_TRY(check_data(q, "q", true));
+  RVA_TRY(check_data(k, "k", true));
+  RVA_TRY(check_data(v, "v", true));
+  memset(p, 0, sizeof(*p));
+  p->x = x;
+  p->x_index = kept_index;
+  p->x_rows = B * N;
+  p->w = w;
+  p->bias = b;
+  p->y[0] = q;
+  p->y[1] = k;
+  p->y[2] = v;
+  p->y_split = 3;
+  p->m_count = cu + B;
+  p->M = B * N;
+  p->K = C;
+  p->Nout = 3 * C;
+  linear_grid(p);
+  return RVA_OK;
+}
+
+int validate_outproj(const void* o, const int32_t* kept_index, const int32_t* cu,
+                     const uint8_t* mask, int B, int N, int C, const void* w, const void* b,
+                     const void* residual, int dtype, void* y, rva::LinearParams* p) {
+  RVA_TRY(check_proj_shape(B, N, C, dtype));
+  RVA_TRY(check_data(o, "o", true));
+  RVA_TRY(check_i32(kept_index, "kept_index", false));
+  RVA_TRY(check_i32(cu, "cu_seqlens", true));
+  if (kept_index && !mask) return fail(RVA_ERR_INVALID, "mask is NULL (needed with kept_index)");
+  RVA_TRY(check_data(w, "w_o", true));
+  RVA_TRY(check_data(b, "b_o", false));
+  RVA_TRY(check_data(residual, "residual", false));
+  RVA_TRY(check_data(y, "y", true));
+  memset(p, 0, sizeof(*p));
+  p->x = o;
+  p->x_rows = B * N;
+  p->w = w;
+  p->bias = b;
+  p->residual = residual;
+  p->y[0] = y;
+  p->y_index = kept_index;
+  p->y_split = 1;
+  p->m_count = cu + B;
+  p->M = B * N;
+  p->K = C;
+  p->Nout = C;
+  if (kept_index) {
+    p->zero_mask = mask;
+    p->zero_rows = B * N;
+  }
+  linear_grid(p);
+  return RVA_OK;
+}
+
+int enqueue_linear(const rva::LinearParams& p, int dtype, hipStream_t s) {
+  hipError_t e = rva::launch_linear(p, dtype, s);
+  if (e != hipSuccess) return hip_fail(e, "projection launch");
+  return RVA_OK;
+}
+
 int enqueue_attend(const rva::AttnParams& p, int dtype, bool fused, hipStream_t s) {
   RVA_TRY(ensure_init());
   hipError_t e = rva::launch_attend(p, dtype, fused, s);
@@ -277,7 +370,7 @@ struct rva_plan_s {
 
 extern "C" {
 
-int rva_version(void) { return 101; }
+int rva_version(void) { return 102; }
 
 const char* rva_status_string(int status) {
   switch (status) {
@@ -331,6 +424,23 @@ int rva_threshold_l2_mask(const void* x, int B, int N, int C, int dtype, double 
   ThreshArgs a;
   RVA_TRY(validate_threshold(x, B, N, C, dtype, keep_quantile, mask_out, &a));
   return enqueue_threshold(a, static_cast<hipStream_t>(stream));
+}
+
+int rva_qkv_projection(const void* x, const int32_t* kept_index, const int32_t* cu_seqlens, int B,
+                       int N, int C, const void* w_qkv, const void* b_qkv, int dtype, void* q,
+                       void* k, void* v, void* stream) {
+  rva::LinearParams p;
+  RVA_TRY(validate_qkv(x, kept_index, cu_seqlens, B, N, C, w_qkv, b_qkv, dtype, q, k, v, &p));
+  return enqueue_linear(p, dtype, static_cast<hipStream_t>(stream));
+}
+
+int rva_out_projection(const void* o, const int32_t* kept_index, const int32_t* cu_seqlens,
+                       const uint8_t* mask, int B, int N, int C, const void* w_o, const void* b_o,
+                       const void* residual, int dtype, void* y, void* stream) {
+  rva::LinearParams p;
+  RVA_TRY(validate_outproj(o, kept_index, cu_seqlens, mask, B, N, C, w_o, b_o, residual, dtype, y,
+                           &p));
+  return enqueue_linear(p, dtype, static_cast<hipStream_t>(stream));
 }
 
 int rva_empty(int count, void* stream) {

@@ -56,6 +56,23 @@ struct ThreshParams {
   int r0;                 // 0-based order statistic a kept patch's norm must reach
 };
 
+struct LinearParams {
+  const void* x;            // input rows, K halves each
+  const int32_t* x_index;   // optional: input row of product row r is x_index[r]
+  int x_rows;               // rows addressable through x
+  const void* w;            // weight [Nout, K]
+  const void* bias;         // [Nout] or NULL
+  const void* residual;     // optional, laid out like y[0] (y_split == 1 only)
+  void* y[3];               // output column groups, [rows, Nout / y_split] each
+  const int32_t* y_index;   // optional: output row of product row r is y_index[r]
+  int y_split;              // number of column groups (1 or 3)
+  const int32_t* m_count;   // optional device count of product rows (clamped to M)
+  int M, K, Nout;           // M: host bound on the product rows
+  int m_tiles, n_tiles;
+  const uint8_t* zero_mask; // optional: rows r < zero_rows of y[0] with zero_mask[r] == 0 are zeroed
+  int zero_rows;
+};
+
 __host__ __device__ inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
 
 inline int attn_kc_max(int dtype) { return dtype == 0 ? kKcMax32 : kKcMax16; }
@@ -87,5 +104,7 @@ hipError_t launch_empty(hipStream_t s);
 hipError_t attend_init();  // raises the dynamic-LDS limit of every attention kernel
 hipError_t launch_threshold(const ThreshParams& p, int B, int dtype, hipStream_t s);
 hipError_t threshold_init();  // raises the dynamic-LDS limit of the keep-mask kernels
+hipError_t launch_linear(const LinearParams& p, int dtype, hipStream_t s);
+int linear_tile_size();
 
 }  // namespace rva

@@ -32,7 +32,8 @@ def test_header_lists_the_entry_points():
     names = _declared()
     for want in ("rva_pack", "rva_ragged_attend", "rva_unpack", "rva_fused", "rva_plan_create",
                  "rva_plan_launch", "rva_plan_destroy", "rva_empty", "rva_status_string",
-                 "rva_last_error", "rva_version", "rva_threshold_l2_mask"):
+                 "rva_last_error", "rva_version", "rva_threshold_l2_mask",
+                 "rva_qkv_projection", "rva_out_projection"):
         assert want in names
 
 
@@ -47,7 +48,7 @@ def test_status_strings(L):
     assert L.rva_status_string(-2) == b"unsupported configuration"
     assert L.rva_status_string(-3) == b"HIP runtime error"
     assert L.rva_status_string(99) == b"unknown status"
-    assert L.rva_version() == 101
+    assert L.rva_version() == 102
 
 
 FAKE = ctypes.c_void_p(0x7F0000000000)  # aligned, never dereferenced: validation fails first
@@ -99,6 +100,25 @@ def test_threshold_validation(L):
     assert thr(q=-0.1) == -1 and thr(q=1.5) == -1 and thr(q=float("nan")) == -1
     assert b"keep_quantile" in L.rva_last_error()
     assert thr(B=1 << 22, N=1024) == -1
+
+
+def test_projection_validation(L):
+    def qkv(x=FAKE, idx=FAKE, cu=FAKE, B=2, N=197, C=768, w=FAKE, b=None, dt=1, q=FAKE):
+        return L.rva_qkv_projection(x, idx, cu, B, N, C, w, b, dt, q, FAKE, FAKE, None)
+    assert qkv(x=None) == -1 and qkv(w=None) == -1 and qkv(q=None) == -1
+    assert qkv(cu=None) == -1 and b"cu_seqlens" in L.rva_last_error()
+    assert qkv(dt=0) == -2 and b"fp16 or bf16" in L.rva_last_error()
+    assert qkv(dt=4) == -1
+    assert qkv(C=100) == -1 and qkv(C=0) == -1 and qkv(C=64 * 65) == -1
+    assert qkv(B=1024, N=1024, C=2048) == -1 and b"2^31" in L.rva_last_error()
+    assert qkv(x=MIS) == -1 and qkv(b=MIS) == -1
+    assert qkv(idx=ctypes.c_void_p(0x7F0000000002)) == -1
+
+    def outp(o=FAKE, idx=FAKE, cu=FAKE, m=FAKE, C=768, w=FAKE, res=None, y=FAKE):
+        return L.rva_out_projection(o, idx, cu, m, 2, 197, C, w, None, res, 1, y, None)
+    assert outp(m=None) == -1 and b"mask" in L.rva_last_error()
+    assert outp(o=None) == -1 and outp(y=None) == -1 and outp(w=None) == -1
+    assert outp(res=MIS) == -1 and outp(C=32) == -1
 
 
 def test_plan_validation(L):
