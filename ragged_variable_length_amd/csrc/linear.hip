@@ -66,108 +66,181 @@ __device__ __forceinline__ u32x2 pack4(float a, float b, float c, float d) {
   }
 }
 
-constexpr int kLinTile = 128;      // output rows and columns per workgroup
+constexpr int kLinBM = 256;        // product rows per workgroup
+constexpr int kLinBN = 256;        // output columns per workgroup
 constexpr int kLinK = 64;          // K per stage
-constexpr int kLinThreads = 256;
+constexpr int kLinStages = 2;      // LDS ring depth (2 or 3)
+constexpr int kLinWM = 4;          // waves along the rows
+constexpr int kLinWN = 4;          // waves along the columns
+constexpr int kLinWaves = kLinWM * kLinWN;
+constexpr int kLinThreads = 64 * kLinWaves;
+constexpr int kLinTM = kLinBM / kLinWM;  // a wave's rows
+constexpr int kLinTN = kLinBN / kLinWN;  // a wave's columns
 constexpr int kLinZeroRows = 64;   // padded rows per zero-fill workgroup
+constexpr int kStageA = kLinBM * 128;  // bytes of one stage's input tile
+constexpr int kStageB = kLinBN * 128;  // bytes of one stage's weight tile
+constexpr int kStageBytes = kStageA + kStageB;
+constexpr int kDmaA = kLinBM / 8 / kLinWaves;  // 1 KB (8-row) loads per wave per stage
+constexpr int kDmaB = kLinBN / 8 / kLinWaves;
+static_assert(kDmaA * 8 * kLinWaves == kLinBM && kDmaB * 8 * kLinWaves == kLinBN, "whole loads");
+constexpr int kDmaPerStage = kDmaA + kDmaB;  // vector memory ops per lane per stage
+static_assert(kDmaPerStage * 2 < 64, "two stages in flight must fit the wait counter");
+static_assert(kLinStages == 2 || kLinStages == 3, "ring depth");
 
-// byte offset of 16-byte piece p of row r in a [128][64] half tile
-__device__ __forceinline__ int lin_swz(int r, int p) { return r * 128 + ((p ^ (r & 7)) << 4); }
+constexpr int kLinGroupRows = 2;   // row blocks per XCD group
+
+// Workgroup slots for the tiles: whole rounds of 8 XCD groups.
+__host__ __device__ inline int linear_tile_slots(int m_tiles, int n_tiles) {
+  const int group = kLinGroupRows * n_tiles;
+  const int groups = (m_tiles * n_tiles + group - 1) / group;
+  return (groups + 7) / 8 * 8 * group;
+}
+
+typedef __attribute__((address_space(3))) void* LdsPtr;
+
+// Swizzle key of row r: piece p of the row is stored at slot p ^ key(r).
+__device__ __forceinline__ int lin_key(int r) { return r & 7; }
+
+// byte offset of 16-byte piece p of row r in a [rows][64] half tile
+__device__ __forceinline__ int lin_swz(int r, int p) { return r * 128 + ((p ^ lin_key(r)) << 4); }
+
+// Wait until at most N vector memory operations of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  // gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt (7) and lgkmcnt (15) left open
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// A workgroup barrier without the full memory fence of __syncthreads (which
+// would also wait for the stages still in flight).  The caller has already
+// waited for the loads other waves must see; this wave's own LDS reads are
+// completed first, because after the barrier other waves refill the buffer
+// they read.  The clobber keeps the compiler from moving LDS accesses across.
+__device__ __forceinline__ void bar() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 template <int DT>
-__device__ __forceinline__ void linear_tile(const LinearParams& p, int mb, int nb,
-                                            unsigned char* lds, int M) {
-  const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
+__device__ __forceinline__ void linear_tile(const LinearParams& p, int mb, int nb, int M,
+                                            unsigned char* buf0, unsigned char* buf1,
+                                            unsigned char* buf2) {
+  const int lane = lane_id(), w = wave_id();
   const int g = lane >> 4, r16 = lane & 15;
-  const int wm = w >> 1, wn = w & 1;  // wave's 64x64 sub-tile
-  const int m0 = mb * kLinTile, n0 = nb * kLinTile;
+  const int wm = w / kLinWN, wn = w - wm * kLinWN;  // wave's kLinTM x kLinTN sub-tile
+  const int m0 = mb * kLinBM, n0 = nb * kLinBN;
   const uint32_t kbytes = (uint32_t)p.K * 2;
   const Rsrc rx = make_rsrc(p.x, (uint32_t)p.x_rows * kbytes);
   const Rsrc rw = make_rsrc(p.w, (uint32_t)p.Nout * kbytes);
 
-  // load roles: pieces e = tid + 256u (u < 4) of each 128-row x 8-piece tile
-  uint32_t arow[4], brow[4];
-  int lrow[4], lpc[4];
+  // Direct-to-LDS loads: one instruction fills 8 rows (1 KB) of a stage, lane
+  // L landing at byte 16 L, i.e. row L / 8, slot L % 8.  The lane fetches the
+  // piece that belongs in that slot under the row swizzle, so LDS ends up in
+  // lin_swz order.  Rows past the product (or the weight) read out of range.
+  const int nkt = p.K / kLinK;
+  uint32_t avoff[kDmaA], bvoff[kDmaB];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int e = tid + kLinThreads * u;
-    lrow[u] = e >> 3;
-    lpc[u] = e & 7;
-    const int m = m0 + lrow[u];
+  for (int i = 0; i < kDmaA; ++i) {
+    const int r = w * (kLinBM / kLinWaves) + 8 * i + (lane >> 3);  // tile row
+    const int m = m0 + r;
     int src = -1;
     if (m < M) src = p.x_index ? p.x_index[m] : m;
-    arow[u] = src >= 0 ? (uint32_t)src * kbytes : kOOB;
-    const int n = n0 + lrow[u];
-    brow[u] = n < p.Nout ? (uint32_t)n * kbytes : kOOB;
+    avoff[i] = src >= 0 ? (uint32_t)src * kbytes + (((lane & 7) ^ lin_key(r)) << 4) : kOOB;
   }
-  auto koff = [&](uint32_t row, int kt, int pc) -> uint32_t {
-    const uint32_t cb = (uint32_t)kt * (kLinK * 2) + (uint32_t)pc * 16;
-    return (row != kOOB && cb < kbytes) ? row + cb : kOOB;
+#pragma unroll
+  for (int i = 0; i < kDmaB; ++i) {
+    const int r = w * (kLinBN / kLinWaves) + 8 * i + (lane >> 3);
+    const int n = n0 + r;
+    bvoff[i] = n < p.Nout ? (uint32_t)n * kbytes + (((lane & 7) ^ lin_key(r)) << 4) : kOOB;
+  }
+  // Stages past the last one are issued anyway (so that every step has the
+  // same loads in flight and the wait counts stay static) through empty
+  // descriptors: every lane is out of range and nothing is read.
+  const Rsrc rnone = make_rsrc(p.x, 0);
+  auto dma = [&](unsigned char* buf, int kt) {
+    const bool live = kt < nkt;
+    const Rsrc ra = live ? rx : rnone, rb = live ? rw : rnone;
+    const int koff = live ? kt * (kLinK * 2) : 0;
+#pragma unroll
+    for (int i = 0; i < kDmaA; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ra, (LdsPtr)(buf + (w * (kLinBM / kLinWaves) + 8 * i) * 128), 16, avoff[i], koff, 0, 0);
+#pragma unroll
+    for (int i = 0; i < kDmaB; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rb, (LdsPtr)(buf + kStageA + (w * (kLinBN / kLinWaves) + 8 * i) * 128), 16, bvoff[i], koff, 0, 0);
   };
 
-  const int nkt = (p.K + kLinK - 1) / kLinK;
-  u32x4 ra[4], rb[4];
+  constexpr int NI = kLinTN / 16, NJ = kLinTM / 16;  // 16x16 blocks of a wave
+  lf32x4 acc[NI][NJ];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    ra[u] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)koff(arow[u], 0, lpc[u]), 0, 0);
-    rb[u] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)koff(brow[u], 0, lpc[u]), 0, 0);
-  }
-  lf32x4 acc[4][4];
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = lf32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NJ; ++j) acc[i][j] = lf32x4{0.f, 0.f, 0.f, 0.f};
 
-  // stage s: A tile at lds + s*32K, W tile at lds + s*32K + 16K
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    *reinterpret_cast<u32x4*>(lds + lin_swz(lrow[u], lpc[u])) = ra[u];
-    *reinterpret_cast<u32x4*>(lds + 16384 + lin_swz(lrow[u], lpc[u])) = rb[u];
-  }
-  __syncthreads();
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int s = kt & 1;
-    // next stage's loads (past the last stage they are out of range: zeros)
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      ra[u] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)koff(arow[u], kt + 1, lpc[u]), 0, 0);
-      rb[u] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)koff(brow[u], kt + 1, lpc[u]), 0, 0);
-    }
-    const unsigned char* As = lds + s * 32768;
-    const unsigned char* Ws = As + 16384;
+  auto compute = [&](const unsigned char* buf) {
+    const unsigned char* As = buf;
+    const unsigned char* Ws = buf + kStageA;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      u32x4 wf[4], xf[4];
+      u32x4 wf[NI];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        wf[i] = *reinterpret_cast<const u32x4*>(Ws + lin_swz(wn * 64 + 16 * i + r16, 4 * ks + g));
-        xf[i] = *reinterpret_cast<const u32x4*>(As + lin_swz(wm * 64 + 16 * i + r16, 4 * ks + g));
+      for (int i = 0; i < NI; ++i)
+        wf[i] = *reinterpret_cast<const u32x4*>(Ws + lin_swz(wn * kLinTN + 16 * i + r16, 4 * ks + g));
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const u32x4 xf = *reinterpret_cast<const u32x4*>(As + lin_swz(wm * kLinTM + 16 * j + r16, 4 * ks + g));
+#pragma unroll
+        for (int i = 0; i < NI; ++i) acc[i][j] = mfma16<DT>(wf[i], xf, acc[i][j]);
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma16<DT>(wf[i], xf[j], acc[i][j]);
     }
-    unsigned char* Nx = lds + (s ^ 1) * 32768;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      *reinterpret_cast<u32x4*>(Nx + lin_swz(lrow[u], lpc[u])) = ra[u];
-      *reinterpret_cast<u32x4*>(Nx + 16384 + lin_swz(lrow[u], lpc[u])) = rb[u];
+  };
+
+  // Three-stage ring, two stages in flight.  Step kt: wait for this wave's
+  // loads of stage kt, barrier (every wave's loads of kt have landed and
+  // every wave is done with stage kt - 1), refill the stage-(kt - 1) buffer
+  // with stage kt + 2, multiply stage kt.  The ring is unrolled so that each
+  // buffer is a distinct LDS object.
+  if constexpr (kLinStages == 3) {
+    auto step = [&](int kt, unsigned char* cur, unsigned char* refill) {
+      wait_vm<kDmaPerStage>();  // stage kt landed; stage kt + 1 may still be in flight
+      bar();
+      dma(refill, kt + 2);
+      if (kt < nkt) compute(cur);
+    };
+    dma(buf0, 0);
+    dma(buf1, 1);
+    for (int kt = 0; kt < nkt; kt += 3) {
+      step(kt, buf0, buf2);
+      step(kt + 1, buf1, buf0);
+      step(kt + 2, buf2, buf1);
     }
-    __syncthreads();
+  } else {
+    // two buffers, one stage in flight: wait for stage kt, barrier (every wave
+    // is done with stage kt - 1), refill its buffer with stage kt + 1, multiply
+    auto step = [&](int kt, unsigned char* cur, unsigned char* refill) {
+      wait_vm<0>();
+      bar();
+      dma(refill, kt + 1);
+      if (kt < nkt) compute(cur);
+    };
+    (void)buf2;
+    dma(buf0, 0);
+    for (int kt = 0; kt < nkt; kt += 2) {
+      step(kt, buf0, buf1);
+      step(kt + 1, buf1, buf0);
+    }
   }
+  wait_vm<0>();
 
   // epilogue: acc[i][j] lane (r16, g) holds out[m][n .. n+3] with
-  // m = m0 + 64 wm + 16 j + r16, n = n0 + 64 wn + 16 i + 4 g
+  // m = m0 + kLinTM wm + 16 j + r16, n = n0 + kLinTN wn + 16 i + 4 g
   const int ng = p.Nout / p.y_split;  // columns per output group
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int m = m0 + wm * 64 + 16 * j + r16;
+  for (int j = 0; j < NJ; ++j) {
+    const int m = m0 + wm * kLinTM + 16 * j + r16;
     if (m >= M) continue;
     const int orow = p.y_index ? p.y_index[m] : m;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int n = n0 + wn * 64 + 16 * i + 4 * g;
+    for (int i = 0; i < NI; ++i) {
+      const int n = n0 + wn * kLinTN + 16 * i + 4 * g;
       if (n >= p.Nout) continue;
       float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
       if (p.bias) {
@@ -205,34 +278,40 @@ __device__ __forceinline__ void linear_zero_rows(const LinearParams& p, int z) {
 }
 
 template <int DT>
-__global__ __launch_bounds__(kLinThreads, 2) void linear_kernel(LinearParams p) {
-  __shared__ __align__(16) unsigned char lds[2 * 32768];
-  const int mt = p.m_tiles, nt = p.n_tiles, tiles = mt * nt;
-  int bid = blockIdx.x;
-  if (bid >= tiles) {
-    linear_zero_rows(p, bid - tiles);
+__global__ __launch_bounds__(kLinThreads, 1) void linear_kernel(LinearParams p) {
+  __shared__ __align__(1024) unsigned char buf0[kStageBytes];
+  __shared__ __align__(1024) unsigned char buf1[kStageBytes];
+  __shared__ __align__(1024) unsigned char buf2[kLinStages == 3 ? kStageBytes : 16];
+  const int nt = p.n_tiles, tiles = p.m_tiles * nt;
+  const int group = kLinGroupRows * nt, slots = linear_tile_slots(p.m_tiles, nt);
+  const int bid = blockIdx.x;
+  if (bid >= slots) {
+    linear_zero_rows(p, bid - slots);
     return;
   }
-  // XCD-aware order: the workgroups dispatched to one XCD (bid = x mod 8)
-  // take consecutive tiles, row block major
-  {
-    const int q8 = tiles >> 3, r8 = tiles & 7, x = bid & 7, s = bid >> 3;
-    bid = (x < r8 ? x * (q8 + 1) : r8 * (q8 + 1) + (x - r8) * q8) + s;
-  }
-  const int mb = bid / nt, nb = bid - mb * nt;
+  // XCD-aware order: tiles are dealt to XCDs (bid = x mod 8) in groups of
+  // kLinGroupRows row blocks x all column tiles, round robin.  A group's input
+  // rows then stay in one XCD's L2 while its column tiles reuse them, and the
+  // live row blocks (those below the device-side row count) spread over all
+  // XCDs whatever that count is.
+  const int x = bid & 7, s = bid >> 3, q = s / group, o = s - q * group;
+  const int t = (q * 8 + x) * group + o;
+  if (t >= tiles) return;
+  const int mb = t / nt, nb = t - mb * nt;
   const int M = p.m_count ? min(*p.m_count, p.M) : p.M;
-  if (mb * kLinTile >= M) return;
-  linear_tile<DT>(p, mb, nb, lds, M);
+  if (mb * kLinBM >= M) return;
+  linear_tile<DT>(p, mb, nb, M, buf0, buf1, buf2);
 }
 
 hipError_t launch_linear(const LinearParams& p, int dtype, hipStream_t s) {
   const int zero_wgs = p.zero_mask ? (p.zero_rows + kLinZeroRows - 1) / kLinZeroRows : 0;
-  const dim3 grid(p.m_tiles * p.n_tiles + zero_wgs);
+  const dim3 grid(linear_tile_slots(p.m_tiles, p.n_tiles) + zero_wgs);
   if (dtype == 1) hipLaunchKernelGGL((linear_kernel<1>), grid, dim3(kLinThreads), 0, s, p);
   else hipLaunchKernelGGL((linear_kernel<2>), grid, dim3(kLinThreads), 0, s, p);
   return hipGetLastError();
 }
 
-int linear_tile_size() { return kLinTile; }
+int linear_tile_rows() { return kLinBM; }
+int linear_tile_cols() { return kLinBN; }
 
 }  // namespace rva

@@ -280,9 +280,9 @@ int check_proj_shape(int B, int N, int C, int dtype) {
 }
 
 void linear_grid(rva::LinearParams* p) {
-  const int t = rva::linear_tile_size();
-  p->m_tiles = (p->M + t - 1) / t;
-  p->n_tiles = (p->Nout + t - 1) / t;
+  const int tm = rva::linear_tile_rows(), tn = rva::linear_tile_cols();
+  p->m_tiles = (p->M + tm - 1) / tm;
+  p->n_tiles = (p->Nout + tn - 1) / tn;
 }
 
 int validate_qkv(const void* x, const int32_t* kept_index, const int32_t* cu, int B, int N, int C,

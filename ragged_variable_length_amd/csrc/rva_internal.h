@@ -105,6 +105,7 @@ hipError_t attend_init();  // raises the dynamic-LDS limit of every attention ke
 hipError_t launch_threshold(const ThreshParams& p, int B, int dtype, hipStream_t s);
 hipError_t threshold_init();  // raises the dynamic-LDS limit of the keep-mask kernels
 hipError_t launch_linear(const LinearParams& p, int dtype, hipStream_t s);
-int linear_tile_size();
+int linear_tile_rows();
+int linear_tile_cols();
 
 }  // namespace rva
