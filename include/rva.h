@@ -251,6 +251,50 @@ int rva_plan_launch(rva_plan plan, void* stream);
 int rva_plan_destroy(rva_plan plan);
 
 /*
+ * Multi-layer plan -- the dispatch argument of the sota2.com Abstract carried
+ * over a stack of layers: ONE pack, then for each of `layers` attention
+ * sub-layers the QKV projection, the ragged attention and the output
+ * projection (residual added in place on the packed stream), then ONE
+ * unpack, all captured as a single graph.  Every layer reuses the same
+ * cu_seqlens (pruning is fixed across the stack: the pages do not say
+ * otherwise).  Layer normalisation and the MLP sub-layer are not part of it.
+ *   x_pad      : [B, N, C] embeddings, C = H * 64; mask: [B, N].
+ *   w_qkv[l], w_o[l] : host arrays of `layers` device pointers ([3C, C] and
+ *                [C, C]); b_qkv / b_o may be NULL, or arrays whose entries
+ *                may be NULL.  The arrays are read at creation only.
+ *   resid, q, k, v, o : packed scratch, [B*N, C] each (capacity).
+ *   cu_seqlens, kept_index : required scratch ([B+1], [B*N]); max_seqlen
+ *                may be NULL.
+ *   y_pad      : [B, N, C] output: the residual stream after the last layer
+ *                at kept positions, +0 at pruned ones.
+ * fp16 / bf16 only.  Launch and destroy with rva_plan_launch / rva_plan_destroy.
+ */
+typedef struct {
+  int B, N, H, d, dtype, layers;
+  int max_seqlen_hint;
+  float softmax_scale;
+  const void* x_pad;
+  const uint8_t* mask;
+  const void* const* w_qkv;
+  const void* const* b_qkv;
+  const void* const* w_o;
+  const void* const* b_o;
+  void* resid;
+  void* q;
+  void* k;
+  void* v;
+  void* o;
+  int32_t* cu_seqlens;
+  int32_t* max_seqlen;
+  int32_t* kept_index;
+  void* y_pad;
+} rva_layers_desc;
+
+#define RVA_MAX_LAYERS 64
+
+int rva_layers_plan_create(const rva_layers_desc* desc, rva_plan* out);
+
+/*
  * rva_empty -- enqueue `count` launches of an empty one-workgroup kernel on
  * `stream` through the same launch path as the entry points above; used to
  * measure the per-launch dispatch floor the Abstract discusses.

@@ -16,7 +16,7 @@ import os
 import torch
 
 __all__ = ["RVAError", "lib", "pack", "ragged_attend", "unpack", "fused", "threshold_l2_mask",
-           "qkv_projection", "out_projection", "index",
+           "qkv_projection", "out_projection", "index", "LayersPlan",
            "Plan", "empty", "dtype_code", "F32", "F16", "BF16", "STAGED", "FUSED", "EMPTY",
            "L2_FUSED", "MAX_TOKENS"]
 
@@ -51,6 +51,19 @@ class _PlanDesc(ctypes.Structure):
                 ("mask_out", ctypes.c_void_p)]
 
 
+class _LayersDesc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int), ("N", ctypes.c_int), ("H", ctypes.c_int), ("d", ctypes.c_int),
+                ("dtype", ctypes.c_int), ("layers", ctypes.c_int), ("max_seqlen_hint", ctypes.c_int),
+                ("softmax_scale", ctypes.c_float), ("x_pad", ctypes.c_void_p),
+                ("mask", ctypes.c_void_p), ("w_qkv", ctypes.POINTER(ctypes.c_void_p)),
+                ("b_qkv", ctypes.POINTER(ctypes.c_void_p)), ("w_o", ctypes.POINTER(ctypes.c_void_p)),
+                ("b_o", ctypes.POINTER(ctypes.c_void_p)), ("resid", ctypes.c_void_p),
+                ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("o", ctypes.c_void_p), ("cu_seqlens", ctypes.c_void_p),
+                ("max_seqlen", ctypes.c_void_p), ("kept_index", ctypes.c_void_p),
+                ("y_pad", ctypes.c_void_p)]
+
+
 _lib = None
 
 
@@ -70,6 +83,7 @@ def lib() -> ctypes.CDLL:
     L.rva_fused.argtypes = [P, P, P, P, I, I, I, I, I, F, I, P, P, P, P]
     L.rva_plan_create.argtypes = [ctypes.POINTER(_PlanDesc), ctypes.POINTER(ctypes.c_void_p)]
     L.rva_plan_launch.argtypes = [P, P]
+    L.rva_layers_plan_create.argtypes = [ctypes.POINTER(_LayersDesc), ctypes.POINTER(ctypes.c_void_p)]
     L.rva_plan_destroy.argtypes = [P]
     L.rva_empty.argtypes = [I, P]
     L.rva_threshold_l2_mask.argtypes = [P, I, I, I, I, ctypes.c_double, P, P]
@@ -82,7 +96,8 @@ def lib() -> ctypes.CDLL:
     L.rva_version.argtypes = []
     for name in ("rva_pack", "rva_ragged_attend", "rva_unpack", "rva_fused", "rva_plan_create",
                  "rva_plan_launch", "rva_plan_destroy", "rva_empty", "rva_version",
-                 "rva_threshold_l2_mask", "rva_qkv_projection", "rva_out_projection"):
+                 "rva_threshold_l2_mask", "rva_qkv_projection", "rva_out_projection",
+                 "rva_layers_plan_create"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -345,3 +360,49 @@ class Plan:
             self.close()
         except Exception:
             pass
+
+
+class LayersPlan(Plan):
+    """One pack, `len(weights)` attention sub-layers (QKV projection, ragged
+    attention, output projection added to the packed residual stream) and one
+    unpack, captured as a single graph.
+
+    x: padded [B,N,C]; mask: [B,N]; weights: list of dicts with w_qkv, b_qkv,
+    w_o, b_o device tensors (biases may be None).  Scratch is allocated here
+    (torch); out (padded [B,N,C]) receives the final residual stream.
+    """
+
+    def __init__(self, x, mask, weights, *, out=None, scale=None, max_seqlen_hint: int = 0):
+        _req(x, "x")
+        B, N, C = x.shape
+        H = C // HEAD_DIM
+        L = len(weights)
+        m = _mask_u8(mask)
+        dev = x.device
+        self.scratch = {nm: torch.empty((B * N, C), dtype=x.dtype, device=dev)
+                        for nm in ("resid", "q", "k", "v", "o")}
+        self.cu_seqlens = torch.empty(B + 1, dtype=torch.int32, device=dev)
+        self.max_seqlen = torch.empty(1, dtype=torch.int32, device=dev)
+        self.kept_index = torch.empty(B * N, dtype=torch.int32, device=dev)
+        self.out = out if out is not None else torch.empty_like(x)
+        self._keep = [x, m, weights, self.scratch, self.out]
+        arr = lambda key: (ctypes.c_void_p * L)(*[
+            (wd[key].data_ptr() if wd.get(key) is not None else None) for wd in weights])
+        self._arrays = {k: arr(k) for k in ("w_qkv", "b_qkv", "w_o", "b_o")}
+        desc = _LayersDesc()
+        desc.B, desc.N, desc.H, desc.d, desc.dtype, desc.layers = B, N, H, HEAD_DIM, dtype_code(x), L
+        desc.max_seqlen_hint = int(max_seqlen_hint)
+        desc.softmax_scale = float(scale or 0.0)
+        desc.x_pad, desc.mask = x.data_ptr(), m.data_ptr()
+        for k, a in self._arrays.items():
+            setattr(desc, k, ctypes.cast(a, ctypes.POINTER(ctypes.c_void_p)))
+        for nm, t in self.scratch.items():
+            setattr(desc, nm, t.data_ptr())
+        desc.cu_seqlens = self.cu_seqlens.data_ptr()
+        desc.max_seqlen = self.max_seqlen.data_ptr()
+        desc.kept_index = self.kept_index.data_ptr()
+        desc.y_pad = self.out.data_ptr()
+        h = ctypes.c_void_p()
+        _check(lib().rva_layers_plan_create(ctypes.byref(desc), ctypes.byref(h)),
+               "rva_layers_plan_create")
+        self._h = h

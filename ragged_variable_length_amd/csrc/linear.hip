@@ -18,15 +18,19 @@
 // T is read on the device (cu_seqlens[B]); the grid is sized for the bound
 // B*N and workgroups past T return at once, so nothing waits on the host.
 //
-// Kernel (gfx950, fp16/bf16 in, fp32 accumulate): 128x128 output tiles,
-// four waves of 64x64, K taken 64 at a time through double-buffered LDS
-// (16-byte pieces XOR-swizzled by row: conflict-free 16-byte operand reads),
-// next K tile loaded into registers while the current one is multiplied.
-// The 16x16x32 matrix-core product is taken transposed, D^T = W X^T, so
-// that each lane ends with four adjacent output columns of one row: one
-// 8-byte store per 16x16 block.  Tiles are ordered so that the workgroups
-// of one XCD walk consecutive row blocks through all column tiles, keeping
-// each input row block in that XCD's L2 while it is reused.
+// Kernel (gfx950, fp16/bf16 in, fp32 accumulate): 256x256 output tiles,
+// sixteen waves of 64x64 (four per SIMD, so one wave's LDS reads hide behind
+// another's matrix-core work), K taken 64 at a time.  Stages reach LDS by
+// direct-to-LDS buffer loads (no staging registers), two buffers deep: the
+// next stage is in flight while the current one is multiplied, and one
+// barrier per stage orders both.  16-byte pieces are XOR-swizzled by row so
+// that the 16-byte operand reads are conflict-free.  The 16x16x32
+// matrix-core product is taken transposed, D^T = W X^T, so that each lane
+// ends with four adjacent output columns of one row: one 8-byte store per
+// 16x16 block.  Tiles are dealt to the XCDs in round-robin groups of two row
+// blocks (all their column tiles), so a group's input rows are reused from
+// one XCD's L2 and the live row blocks (below the device-side row count)
+// spread over every XCD.
 #include "rva_device.h"
 #include "rva_internal.h"
 

@@ -9,6 +9,7 @@
 
 #include <mutex>
 #include <new>
+#include <vector>
 
 #include "rva.h"
 #include "rva_internal.h"
@@ -368,9 +369,50 @@ struct rva_plan_s {
   hipGraphExec_t exec;
 };
 
+namespace {
+
+// Captures the launches `enqueue(stream)` makes on a private stream and
+// instantiates them as a plan.  Nothing runs on the device here.
+template <typename F>
+int capture_plan(rva_plan* out, F enqueue) {
+  hipStream_t cs = nullptr;
+  hipError_t e = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking);
+  if (e != hipSuccess) return hip_fail(e, "capture stream");
+  e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+  if (e != hipSuccess) {
+    (void)hipStreamDestroy(cs);
+    return hip_fail(e, "begin capture");
+  }
+  const int st = enqueue(cs);
+  hipGraph_t graph = nullptr;
+  hipError_t ee = hipStreamEndCapture(cs, &graph);
+  (void)hipStreamDestroy(cs);
+  if (st != RVA_OK) {
+    if (graph) (void)hipGraphDestroy(graph);
+    return st;
+  }
+  if (ee != hipSuccess) return hip_fail(ee, "end capture");
+  hipGraphExec_t exec = nullptr;
+  e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+  if (e != hipSuccess) {
+    (void)hipGraphDestroy(graph);
+    return hip_fail(e, "graph instantiate");
+  }
+  rva_plan_s* plan = new (std::nothrow) rva_plan_s{graph, exec};
+  if (!plan) {
+    (void)hipGraphExecDestroy(exec);
+    (void)hipGraphDestroy(graph);
+    return fail(RVA_ERR_INVALID, "out of host memory");
+  }
+  *out = plan;
+  return RVA_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
-int rva_version(void) { return 102; }
+int rva_version(void) { return 103; }
 
 const char* rva_status_string(int status) {
   switch (status) {
@@ -490,17 +532,10 @@ int rva_plan_create(const rva_plan_desc* desc, rva_plan* out) {
       return fail(RVA_ERR_INVALID, "unknown plan mode %d", D.mode);
   }
   RVA_TRY(ensure_init());
-
-  hipStream_t cs = nullptr;
-  hipError_t e = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking);
-  if (e != hipSuccess) return hip_fail(e, "capture stream");
-  e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
-  if (e != hipSuccess) {
-    (void)hipStreamDestroy(cs);
-    return hip_fail(e, "begin capture");
-  }
-  int st = RVA_OK;
-  switch (D.mode) {
+  return capture_plan(out, [&](hipStream_t cs) -> int {
+    hipError_t e;
+    int st = RVA_OK;
+    switch (D.mode) {
     case RVA_PLAN_STAGED:
       st = enqueue_pack(pack, cs);
       if (st == RVA_OK) st = enqueue_attend(attn, D.dtype, false, cs);
@@ -520,29 +555,51 @@ int rva_plan_create(const rva_plan_desc* desc, rva_plan* out) {
       e = rva::launch_empty(cs);
       if (e != hipSuccess) st = hip_fail(e, "empty launch");
       break;
-  }
-  hipGraph_t graph = nullptr;
-  hipError_t ee = hipStreamEndCapture(cs, &graph);
-  (void)hipStreamDestroy(cs);
-  if (st != RVA_OK) {
-    if (graph) (void)hipGraphDestroy(graph);
+    }
     return st;
+  });
+}
+
+int rva_layers_plan_create(const rva_layers_desc* desc, rva_plan* out) {
+  if (!desc || !out) return fail(RVA_ERR_INVALID, "desc and out must be non-NULL");
+  *out = nullptr;
+  const rva_layers_desc& D = *desc;
+  const int L = D.layers;
+  if (L < 1 || L > RVA_MAX_LAYERS)
+    return fail(RVA_ERR_INVALID, "layers must be in [1, %d] (got %d)", RVA_MAX_LAYERS, L);
+  if (!D.w_qkv || !D.w_o) return fail(RVA_ERR_INVALID, "w_qkv and w_o arrays are required");
+  RVA_TRY(check_shape(D.B, D.N, D.H, D.d, D.dtype));
+  const int C = D.H * D.d;
+  if (!D.kept_index) return fail(RVA_ERR_INVALID, "kept_index is NULL");
+  // one pack of x into the residual stream, L x (qkv, attention, out + residual), one unpack
+  PackArgs pack, unpack;
+  RVA_TRY(validate_pack(D.x_pad, nullptr, nullptr, D.mask, D.B, D.N, D.H, D.d, D.dtype, D.resid,
+                        nullptr, nullptr, D.cu_seqlens, D.max_seqlen, D.kept_index, &pack));
+  RVA_TRY(validate_unpack(D.resid, D.cu_seqlens, D.mask, D.B, D.N, D.H, D.d, D.dtype, D.y_pad,
+                          &unpack));
+  std::vector<rva::LinearParams> qkv(L), outp(L);
+  rva::AttnParams attn;
+  RVA_TRY(validate_attend(D.q, D.k, D.v, D.cu_seqlens, D.B, D.H, D.d,
+                          D.max_seqlen_hint > 0 ? D.max_seqlen_hint : D.N, D.softmax_scale,
+                          D.dtype, D.o, &attn));
+  for (int l = 0; l < L; ++l) {
+    RVA_TRY(validate_qkv(D.resid, nullptr, D.cu_seqlens, D.B, D.N, C, D.w_qkv[l],
+                         D.b_qkv ? D.b_qkv[l] : nullptr, D.dtype, D.q, D.k, D.v, &qkv[l]));
+    RVA_TRY(validate_outproj(D.o, nullptr, D.cu_seqlens, D.mask, D.B, D.N, C, D.w_o[l],
+                             D.b_o ? D.b_o[l] : nullptr, D.resid, D.dtype, D.resid, &outp[l]));
   }
-  if (ee != hipSuccess) return hip_fail(ee, "end capture");
-  hipGraphExec_t exec = nullptr;
-  e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
-  if (e != hipSuccess) {
-    (void)hipGraphDestroy(graph);
-    return hip_fail(e, "graph instantiate");
-  }
-  rva_plan_s* plan = new (std::nothrow) rva_plan_s{graph, exec};
-  if (!plan) {
-    (void)hipGraphExecDestroy(exec);
-    (void)hipGraphDestroy(graph);
-    return fail(RVA_ERR_INVALID, "out of host memory");
-  }
-  *out = plan;
-  return RVA_OK;
+  RVA_TRY(ensure_init());
+  return capture_plan(out, [&](hipStream_t cs) -> int {
+    RVA_TRY(enqueue_pack(pack, cs));
+    for (int l = 0; l < L; ++l) {
+      RVA_TRY(enqueue_linear(qkv[l], D.dtype, cs));
+      RVA_TRY(enqueue_attend(attn, D.dtype, false, cs));
+      RVA_TRY(enqueue_linear(outp[l], D.dtype, cs));
+    }
+    hipError_t e = rva::launch_unpack(unpack.cp, unpack.splits, cs);
+    if (e != hipSuccess) return hip_fail(e, "unpack launch");
+    return RVA_OK;
+  });
 }
 
 int rva_plan_launch(rva_plan plan, void* stream) {

@@ -46,3 +46,33 @@ def max_err(got: np.ndarray, ref: np.ndarray) -> float:
         return 0.0
     assert np.isfinite(got).all(), "non-finite value in device output"
     return float(np.abs(got - ref).max())
+
+
+# Projection tolerance, derived from the arithmetic: products of two 16-bit
+# values are exact in fp32, the K-term sum is accumulated in fp32 (error at
+# most (K + 2) 2^-24 times the sum of |terms|, bias and residual included),
+# and the result is rounded once to the output type (half an ulp: 2^-11
+# relative for fp16, 2^-8 for bf16, plus fp16's subnormal spacing near zero).
+U_OUT = {"f16": 2.0 ** -11, "bf16": 2.0 ** -8}
+ABS_FLOOR = {"f16": 2.0 ** -24, "bf16": 2.0 ** -133}
+
+
+def linear_bound(xs, w, b, r, dtype=None):
+    """Accumulation part of the bound for y = xs w^T + b + r (fp64 decoded);
+    the same for every 16-bit input type."""
+    K = xs.shape[1]
+    mag = np.abs(xs) @ np.abs(w).T
+    if b is not None:
+        mag = mag + np.abs(b)
+    if r is not None:
+        mag = mag + np.abs(r)
+    return mag * (K + 2) * 2.0 ** -24
+
+
+def check_linear(got, ref, mag_bound, dtype, what):
+    """Every element within its own bound."""
+    tol = U_OUT[dtype] * np.abs(ref) + mag_bound * (1 + U_OUT[dtype]) + ABS_FLOOR[dtype]
+    err = np.abs(got - ref)
+    assert np.isfinite(got).all(), what
+    bad = err > tol
+    assert not bad.any(), (what, float(err.max()), np.argwhere(bad)[:4])

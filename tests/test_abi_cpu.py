@@ -33,7 +33,7 @@ def test_header_lists_the_entry_points():
     for want in ("rva_pack", "rva_ragged_attend", "rva_unpack", "rva_fused", "rva_plan_create",
                  "rva_plan_launch", "rva_plan_destroy", "rva_empty", "rva_status_string",
                  "rva_last_error", "rva_version", "rva_threshold_l2_mask",
-                 "rva_qkv_projection", "rva_out_projection"):
+                 "rva_qkv_projection", "rva_out_projection", "rva_layers_plan_create"):
         assert want in names
 
 
@@ -48,7 +48,7 @@ def test_status_strings(L):
     assert L.rva_status_string(-2) == b"unsupported configuration"
     assert L.rva_status_string(-3) == b"HIP runtime error"
     assert L.rva_status_string(99) == b"unknown status"
-    assert L.rva_version() == 102
+    assert L.rva_version() == 103
 
 
 FAKE = ctypes.c_void_p(0x7F0000000000)  # aligned, never dereferenced: validation fails first
@@ -119,6 +119,30 @@ def test_projection_validation(L):
     assert outp(m=None) == -1 and b"mask" in L.rva_last_error()
     assert outp(o=None) == -1 and outp(y=None) == -1 and outp(w=None) == -1
     assert outp(res=MIS) == -1 and outp(C=32) == -1
+
+
+def test_layers_plan_validation(L):
+    import ragged_variable_length_amd as rva
+    d = rva._LayersDesc()
+    h = ctypes.c_void_p()
+    assert L.rva_layers_plan_create(None, ctypes.byref(h)) == -1
+    d.B, d.N, d.H, d.d, d.dtype, d.layers = 2, 197, 12, 64, 1, 0
+    assert L.rva_layers_plan_create(ctypes.byref(d), ctypes.byref(h)) == -1
+    assert b"layers" in L.rva_last_error()
+    d.layers = 65
+    assert L.rva_layers_plan_create(ctypes.byref(d), ctypes.byref(h)) == -1
+    d.layers = 2
+    assert L.rva_layers_plan_create(ctypes.byref(d), ctypes.byref(h)) == -1  # no weight arrays
+    assert b"w_qkv" in L.rva_last_error()
+    arr = (ctypes.c_void_p * 2)(0x7F0000000000, None)  # second layer's weight missing
+    d.w_qkv = d.w_o = ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
+    for f in ("x_pad", "mask", "resid", "q", "k", "v", "o", "cu_seqlens", "kept_index", "y_pad"):
+        setattr(d, f, 0x7F0000000000)
+    assert L.rva_layers_plan_create(ctypes.byref(d), ctypes.byref(h)) == -1
+    assert b"w_qkv" in L.rva_last_error()
+    d.dtype = 0
+    assert L.rva_layers_plan_create(ctypes.byref(d), ctypes.byref(h)) == -2
+    assert h.value is None
 
 
 def test_plan_validation(L):

@@ -1,11 +1,6 @@
-"""QKV and output projections on the device against the fp64 oracle.
-
-Tolerance, derived from the arithmetic: products of two 16-bit values are
-exact in fp32, the K-term sum is accumulated in fp32 (error at most
-(K + 2) 2^-24 times the sum of |terms|, bias and residual included), and the
-result is rounded once to the output type (half an ulp: 2^-11 relative for
-fp16, 2^-8 for bf16, plus fp16's subnormal spacing near zero).  Every element
-is checked against its own bound."""
+"""QKV and output projections on the device against the fp64 oracle.  Every
+element is checked against its own bound derived from the arithmetic
+(gpu_util.linear_bound / check_linear)."""
 import sys
 
 import numpy as np
@@ -17,10 +12,10 @@ import workloads as W
 pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
-from gpu_util import TOL, f64, max_err, to_dev  # noqa: E402
+from gpu_util import TOL, check_linear, f64, linear_bound, max_err, to_dev  # noqa: E402
 
-U_OUT = {"f16": 2.0 ** -11, "bf16": 2.0 ** -8}
-ABS_FLOOR = {"f16": 2.0 ** -24, "bf16": 2.0 ** -133}
+_bound = linear_bound
+_check = check_linear
 
 
 def _rva():
@@ -32,25 +27,6 @@ def _rva():
 def _say(*a):
     print(*a, flush=True)
     sys.stdout.flush()
-
-
-def _bound(xs, w, b, r, dtype):
-    """Per-element bound for y = xs w^T + b + r (all fp64 decoded)."""
-    K = xs.shape[1]
-    mag = np.abs(xs) @ np.abs(w).T
-    if b is not None:
-        mag = mag + np.abs(b)
-    if r is not None:
-        mag = mag + np.abs(r)
-    return mag * (K + 2) * 2.0 ** -24
-
-
-def _check(got, ref, mag_bound, dtype, what):
-    tol = U_OUT[dtype] * np.abs(ref) + mag_bound * (1 + U_OUT[dtype]) + ABS_FLOOR[dtype]
-    err = np.abs(got - ref)
-    assert np.isfinite(got).all(), what
-    bad = err > tol
-    assert not bad.any(), (what, float(err.max()), np.argwhere(bad)[:4])
 
 
 def _mask(seed, B, N, lo=0.0, hi=1.0, empty_image=False):
