@@ -267,6 +267,78 @@ def measure_threshold(ctx, reps):
     return res
 
 
+def measure_block(ctx, reps, layers=12):
+    """The attention block around the ragged path at DeiT-B width on the mixed
+    batch (synthetic weights): stage by stage (offsets and kept index, QKV
+    gather-product, ragged attention, output product with scatter), then a
+    `layers`-deep stack as one multi-layer plan, ragged and padded-dense."""
+    import numpy as np
+    import workloads as W
+    t, rva = ctx.torch, ctx.rva
+    w = W.mixed_peak()
+    B, N, H = w.B, w.N, w.H
+    C = H * 64
+    T = w.total_kept
+    x = t.from_numpy(W.embeddings(B=B, N=N, C=C)).to(ctx.dev)
+    md = t.from_numpy(w.mask).to(ctx.dev)
+
+    def weights(seed):
+        return {k: t.from_numpy(v).to(ctx.dev) for k, v in W.projection_weights(seed=seed, C=C).items()}
+    wd = weights(2000)
+    idx = rva.index(md)
+    cu = idx["cu_seqlens"]
+    qkv = tuple(t.empty((B * N, C), dtype=t.float16, device=ctx.dev) for _ in range(3))
+    o = t.empty((B * N, C), dtype=t.float16, device=ctx.dev)
+    y = t.empty((B, N, C), dtype=t.float16, device=ctx.dev)
+    q, k, v = qkv
+    stages = {
+        "index": (lambda: rva.index(md, out=idx), 0),
+        "qkv_projection": (lambda: rva.qkv_projection(x, cu, wd["w_qkv"], wd["b_qkv"],
+                                                      kept_index=idx["kept_index"], out=qkv),
+                           2 * T * C * 3 * C),
+        "ragged_attention": (lambda: rva.ragged_attend(q.view(-1, H, 64), k.view(-1, H, 64),
+                                                       v.view(-1, H, 64), cu, 197,
+                                                       out=o.view(-1, H, 64)),
+                             4 * 64 * H * int((w.counts.astype(np.int64) ** 2).sum())),
+        "out_projection": (lambda: rva.out_projection(o, cu, wd["w_o"], wd["b_o"],
+                                                      kept_index=idx["kept_index"], mask=md, out=y),
+                           2 * T * C * C),
+    }
+    res = {"workload": w.name, "C": C, "T": T, "stages": {}}
+    total = 0.0
+    for name, (fn, flops) in stages.items():
+        for _ in range(3):
+            fn()
+        us = ctx.events_time(fn, reps)
+        total += us
+        e = {"kernel_us_warm": round(us, 2)}
+        if flops:
+            e["TFLOPs"] = round(flops / (us * 1e-6) / 1e12, 1)
+            e["mfma_frac"] = round(flops / (us * 1e-6) / 1e12 / MFMA_PEAK_TFLOPS["f16"], 4)
+        res["stages"][name] = e
+    res["block_us"] = round(total, 2)
+    res["attention_share"] = round(res["stages"]["ragged_attention"]["kernel_us_warm"] / total, 4)
+    del qkv, q, k, v, o, y
+    # the stack, ragged and padded-dense (every token kept)
+    wl = [weights(2100 + l) for l in range(layers)]
+    out = {}
+    for label, mask in (("ragged", md), ("padded_dense", t.ones_like(md))):
+        plan = rva.LayersPlan(x, mask, wl, max_seqlen_hint=197)
+        for _ in range(2):
+            plan.launch()
+        us = ctx.events_time(plan.launch, max(3, reps // 10))
+        kept = T if label == "ragged" else B * N
+        out[label] = {"us": round(us, 1), "us_per_layer": round(us / layers, 1),
+                      "kept_tokens_per_s": round(kept / (us * 1e-6))}
+        plan.close()
+        del plan
+        t.cuda.empty_cache()
+    out["layers"] = layers
+    out["ragged_speedup"] = round(out["padded_dense"]["us"] / out["ragged"]["us"], 3)
+    res["stack"] = out
+    return res
+
+
 def measure_floor(ctx, reps):
     rva = ctx.rva
     plan = rva.Plan(rva.EMPTY)
@@ -511,6 +583,9 @@ def main():
         line["per_config"] = per
         log("measuring the keep-mask ...")
         line["threshold_l2"] = measure_threshold(ctx, reps)
+        log("measuring the attention block and the layer stack ...")
+        line["attention_block"] = measure_block(ctx, 50)
+        torch.cuda.empty_cache()
     if not args.no_cpu:
         log("timing the CPU oracle ...")
         line["cpu_baseline"] = cpu_baseline(w)
