@@ -127,6 +127,22 @@ int rva_fused(const void* q_pad, const void* k_pad, const void* v_pad, const uin
               void* o_pad, int32_t* cu_seqlens, int32_t* max_seqlen, void* stream);
 
 /*
+ * rva_fused_persistent -- rva_fused as a persistent grid: as many workgroups
+ * as stay resident, each pulling (image, head) items from a device counter,
+ * fetching the next item's mask row while it works on the current one.
+ * Same arguments and results as rva_fused (16-bit inputs; fp32 falls back to
+ * rva_fused), plus:
+ *   work : int32[2] device scratch, all zero before the first call.  Every
+ *          call leaves it zero again when it completes, so one buffer serves
+ *          any number of stream-ordered calls; calls that may run at the same
+ *          time need distinct buffers.
+ */
+int rva_fused_persistent(const void* q_pad, const void* k_pad, const void* v_pad,
+                         const uint8_t* mask, int B, int N, int H, int d, int max_seqlen_hint,
+                         float softmax_scale, int dtype, void* o_pad, int32_t* cu_seqlens,
+                         int32_t* max_seqlen, int32_t* work, void* stream);
+
+/*
  * rva_threshold_l2_mask -- the Threshold-l2 keep-mask that feeds the path
  * (one of the four pruning algorithms the aissential.tech summary lists in
  * its "Summary"; the pages give no definition, the reading below is this
@@ -203,6 +219,9 @@ int rva_out_projection(const void* o, const int32_t* kept_index, const int32_t* 
  *      RVA_PLAN_L2_FUSED : rva_threshold_l2_mask from x into mask_out, then
  *                        rva_fused reading mask_out (2 kernels); `mask` is
  *                        ignored.
+ *      RVA_PLAN_PERSISTENT : rva_fused_persistent (1 kernel); the plan owns
+ *                        its work counter (8 bytes of device memory,
+ *                        allocated and zeroed at creation, freed at destroy).
  * Every pointer and size is fixed at creation; the CONTENTS of the inputs
  * (including the mask) may change between launches.  Staged mode needs the
  * packed scratch buffers q/k/v/o_packed (capacity B*N rows each) and
@@ -216,7 +235,8 @@ typedef enum {
   RVA_PLAN_STAGED = 0,
   RVA_PLAN_FUSED = 1,
   RVA_PLAN_EMPTY = 2,
-  RVA_PLAN_L2_FUSED = 3
+  RVA_PLAN_L2_FUSED = 3,
+  RVA_PLAN_PERSISTENT = 4
 } rva_plan_mode;
 
 typedef struct {

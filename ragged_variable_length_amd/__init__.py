@@ -16,7 +16,8 @@ import os
 import torch
 
 __all__ = ["RVAError", "lib", "pack", "ragged_attend", "unpack", "fused", "threshold_l2_mask",
-           "qkv_projection", "out_projection", "index", "LayersPlan",
+           "qkv_projection", "out_projection", "index", "LayersPlan", "fused_persistent",
+           "PERSISTENT",
            "Plan", "empty", "dtype_code", "F32", "F16", "BF16", "STAGED", "FUSED", "EMPTY",
            "L2_FUSED", "MAX_TOKENS"]
 
@@ -24,7 +25,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "librva.so")
 
 F32, F16, BF16 = 0, 1, 2
-STAGED, FUSED, EMPTY, L2_FUSED = 0, 1, 2, 3
+STAGED, FUSED, EMPTY, L2_FUSED, PERSISTENT = 0, 1, 2, 3, 4
 MAX_TOKENS = 1024
 HEAD_DIM = 64
 
@@ -81,6 +82,7 @@ def lib() -> ctypes.CDLL:
     L.rva_ragged_attend.argtypes = [P, P, P, P, I, I, I, I, F, I, P, P]
     L.rva_unpack.argtypes = [P, P, P, I, I, I, I, I, P, P]
     L.rva_fused.argtypes = [P, P, P, P, I, I, I, I, I, F, I, P, P, P, P]
+    L.rva_fused_persistent.argtypes = [P, P, P, P, I, I, I, I, I, F, I, P, P, P, P, P]
     L.rva_plan_create.argtypes = [ctypes.POINTER(_PlanDesc), ctypes.POINTER(ctypes.c_void_p)]
     L.rva_plan_launch.argtypes = [P, P]
     L.rva_layers_plan_create.argtypes = [ctypes.POINTER(_LayersDesc), ctypes.POINTER(ctypes.c_void_p)]
@@ -97,7 +99,7 @@ def lib() -> ctypes.CDLL:
     for name in ("rva_pack", "rva_ragged_attend", "rva_unpack", "rva_fused", "rva_plan_create",
                  "rva_plan_launch", "rva_plan_destroy", "rva_empty", "rva_version",
                  "rva_threshold_l2_mask", "rva_qkv_projection", "rva_out_projection",
-                 "rva_layers_plan_create"):
+                 "rva_layers_plan_create", "rva_fused_persistent"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -234,6 +236,23 @@ def fused(q, k, v, mask, *, max_seqlen_hint: int = 0, scale: float | None = None
     _check(lib().rva_fused(_ptr(q), _ptr(k), _ptr(v), _ptr(m), B, N, H, d, int(max_seqlen_hint),
                            float(scale or 0.0), dtype_code(q), _ptr(out), _ptr(cu_seqlens),
                            _ptr(max_seqlen), _stream(stream)), "rva_fused")
+    return out
+
+
+def fused_persistent(q, k, v, mask, work, *, max_seqlen_hint: int = 0, scale: float | None = None,
+                     out=None, cu_seqlens=None, max_seqlen=None, stream=None):
+    """fused() as a persistent grid.  work: int32 [2] device tensor, zero
+    before the first call (every call leaves it zero again)."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _req(t, name)
+    m = _mask_u8(mask)
+    B, N, H, d = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    _check(lib().rva_fused_persistent(_ptr(q), _ptr(k), _ptr(v), _ptr(m), B, N, H, d,
+                                      int(max_seqlen_hint), float(scale or 0.0), dtype_code(q),
+                                      _ptr(out), _ptr(cu_seqlens), _ptr(max_seqlen), _ptr(work),
+                                      _stream(stream)), "rva_fused_persistent")
     return out
 
 

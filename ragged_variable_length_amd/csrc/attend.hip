@@ -7,8 +7,10 @@
 // Work decomposition (CDNA4 / gfx950), 16-bit inputs:
 //  * one workgroup of 4 waves per (image, head).  Post-pruning ViT sequences
 //    are short (at most 197 tokens at 224x224, 577 at 384x384), so the
-//    workgroup stages its sequence's K and V (V transposed) in LDS in one
-//    memory round trip; sequences longer than one chunk are staged in chunks;
+//    workgroup stages its sequence's K and V in LDS in one memory round trip,
+//    by direct-to-LDS loads; sequences longer than one chunk are staged in
+//    chunks.  V stays row-major and the V^T operand comes from the
+//    transposed LDS read;
 //  * each wave owns two query blocks of 16 rows at a time and walks the keys
 //    32 at a time;
 //  * scores are formed transposed, S^T = K Q^T, with the 16x16x32 matrix-core
@@ -155,16 +157,19 @@ __device__ __forceinline__ void softmax_step16(f32x4& s0, f32x4& s1, int kvalid,
 
 // ---------------------------------------------------------------- 16-bit
 
-// Staged K is [kc][64] halves with the eight 16-byte pieces of row r stored
-// at piece index p ^ (r & 7): the 16 rows a b128 fragment read touches then
-// spread over all banks without padding.
-__device__ __forceinline__ int kswz(int row, int piece) { return row * 64 + ((piece ^ (row & 7)) << 3); }
+// Staged K and V are row-major [kc][64] halves (128-byte rows) with the
+// eight 16-byte pieces of row r stored at slot p ^ (r & 7): the rows one
+// fragment read touches then spread over the banks without padding.
+__device__ __forceinline__ int kvswz(int row, int piece) { return row * 128 + ((piece ^ (row & 7)) << 4); }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 LdsS16x4;
 
 template <int DT>
-__device__ __forceinline__ void tile16(const typename Half16<DT>::T* __restrict__ Ks,
-                                       const typename Half16<DT>::T* __restrict__ Vt, int VP, int k0,
-                                       int kvalid, const typename Half16<DT>::V8 (&qf)[2][2],
-                                       f32x4 (&o)[2][5], float (&m)[2], bool two, float c) {
+__device__ __forceinline__ void tile16(const unsigned char* __restrict__ Ks,
+                                       const unsigned char* __restrict__ Vs, int k0, int kvalid,
+                                       const typename Half16<DT>::V8 (&qf)[2][2], f32x4 (&o)[2][5],
+                                       float (&m)[2], bool two, float c) {
   typedef Half16<DT> Tr;
   typedef typename Tr::T T;
   typedef typename Tr::V8 V8;
@@ -176,13 +181,22 @@ __device__ __forceinline__ void tile16(const typename Half16<DT>::T* __restrict_
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
-      kf[kb][ks] = *reinterpret_cast<const V8*>(Ks + kswz(k0 + kb * 16 + r16, ks * 4 + g));
+      kf[kb][ks] = *reinterpret_cast<const V8*>(Ks + kvswz(k0 + kb * 16 + r16, ks * 4 + g));
+  // A operand of O^T = V^T P^T: lane (r16, g) holds V[key][16 db + r16] for
+  // keys k0 + 4g + j and k0 + 16 + 4g + j (j < 4), the keys whose
+  // probabilities this lane's column of P^T carries.  The transposed LDS read
+  // hands lane i of a 16-lane group element i % 4 of the 8-byte pieces
+  // addressed by the group's lanes 4k + i / 4 (k < 4), so lane s addresses key
+  // row k0 + 4g + s / 4 at dims 16 db + 4 (s % 4) .. + 3.
+  const int trow = k0 + 4 * g + (r16 >> 2), tcol = r16 & 3;
   V8 vf[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) {
-    const T* row = Vt + (db * 16 + r16) * VP + k0 + 4 * g;
-    const V4 lo = *reinterpret_cast<const V4*>(row);
-    const V4 hi = *reinterpret_cast<const V4*>(row + 16);
+    const int piece = 2 * db + (tcol >> 1), half = (tcol & 1) << 3;
+    const V4 lo = __builtin_bit_cast(V4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (LdsS16x4*)(Vs + kvswz(trow, piece) + half)));
+    const V4 hi = __builtin_bit_cast(V4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (LdsS16x4*)(Vs + kvswz(trow + 16, piece) + half)));
     vf[db] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   }
 #pragma unroll
@@ -213,82 +227,60 @@ __device__ __forceinline__ void tile16(const typename Half16<DT>::T* __restrict_
 // (make_rsrc) whose base is the sequence's head slice and whose size covers
 // exactly its rows, so ragged tails need no branches.
 
-// Stage keys [c0, c0 + rows) of the sequence: K rows into Ks (swizzled
-// 16-byte pieces), V transposed into Vt[d][key].  Every load of the chunk is
-// issued before the first LDS store, so one memory round trip stages the
-// whole chunk.  The V^T block of an item is 4 keys x 4 dims: four 8-byte row
-// loads (16 lanes cover one 128-byte row), a 4x4 transpose of 16-bit values
-// in registers, four 8-byte LDS stores.  Keys in [rows, round_up(rows, 32))
-// load as zeros, so masked probabilities (exact zeros) never meet stale LDS
-// contents.  `roff(r)` is the byte offset of sequence row r.
+// Stage keys [c0, c0 + rows) of the sequence: K and V rows into Ks / Vs by
+// direct-to-LDS buffer loads (no registers, no LDS stores by the waves).
+// One load instruction fills 8 rows (1 KB), lane L landing at byte 16 L,
+// i.e. row L / 8, slot L % 8; the lane fetches the 16-byte piece that the
+// row swizzle puts in that slot.  Every row offset is read (through roff)
+// before the first load is issued, so no load waits behind another's LDS
+// write.  Keys in [rows, round_up(rows, 32)) are out of range and land as
+// zeros, so masked probabilities (exact zeros) never meet stale LDS
+// contents.  The caller's barrier (with its memory fence) makes the chunk
+// visible.  `roff(r)` is the byte offset of sequence row r.
 template <int DT, typename RowOff>
-__device__ __forceinline__ void stage16(Rsrc rk, Rsrc rv, typename Half16<DT>::T* Ks,
-                                        typename Half16<DT>::T* Vt, int VP, int c0, int rows,
-                                        RowOff roff) {
-  constexpr int NT = kAttnThreads16;
-  constexpr int UK = (kKcMax16 * 8 + NT - 1) / NT;       // K pieces per thread at most
-  constexpr int UV = (kKcMax16 / 4 * 16 + NT - 1) / NT;  // V^T blocks per thread at most
-  static_assert(kKcMax16 % kKeyTile == 0, "chunks are whole key tiles");
-  const int tid = threadIdx.x;
+__device__ __forceinline__ void stage16(Rsrc rk, Rsrc rv, unsigned char* Ks, unsigned char* Vs,
+                                        int c0, int rows, RowOff roff) {
+  constexpr int kWaves = kAttnThreads16 / 64;
+  constexpr int NI = kKcMax16 / 8 / kWaves;  // 8-row loads per wave, at most
+  static_assert(kKcMax16 % (8 * kWaves) == 0 && kKcMax16 % kKeyTile == 0, "whole loads");
+  const int lane = lane_id(), w = wave_id();
   const int rpad = round_up(rows, kKeyTile);
-  const int kitems = rpad * 8, vitems = rpad / 4 * 16;
-  u32x4 kr[UK];
-  u32x2 vr[UV][4];
+  const int rl = lane >> 3;                 // row within the load (row & 7 == rl)
+  const uint32_t piece16 = (uint32_t)(((lane & 7) ^ rl) << 4);
+  uint32_t off[NI];
 #pragma unroll
-  for (int u = 0; u < UK; ++u) {
-    const int e = tid + u * NT;
-    const int r = e >> 3, pc = e & 7;
-    const uint32_t o = (e < kitems && r < rows) ? roff(c0 + r) + pc * 16 : kOOB;
-    kr[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)o, 0, 0);
+  for (int i = 0; i < NI; ++i) {
+    const int r = 8 * (w + kWaves * i) + rl;
+    off[i] = r < rows ? roff(c0 + r) + piece16 : kOOB;
   }
 #pragma unroll
-  for (int u = 0; u < UV; ++u) {
-    const int it = tid + u * NT;
-    const int kq = it >> 4, dq = it & 15;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int key = 4 * kq + j;
-      const uint32_t o = (it < vitems && key < rows) ? roff(c0 + key) + dq * 8 : kOOB;
-      vr[u][j] = __builtin_amdgcn_raw_buffer_load_b64(rv, (int)o, 0, 0);
-    }
-  }
-#pragma unroll
-  for (int u = 0; u < UK; ++u) {
-    const int e = tid + u * NT;
-    if (e < kitems) *reinterpret_cast<u32x4*>(Ks + kswz(e >> 3, e & 7)) = kr[u];
-  }
-  char* vt = reinterpret_cast<char*>(Vt);
-#pragma unroll
-  for (int u = 0; u < UV; ++u) {
-    const int it = tid + u * NT;
-    if (it >= vitems) continue;
-    const int kq = it >> 4, dq = it & 15;
-    // vr[u][j] holds V[key 4kq+j][dims 4dq..4dq+3]; out holds V^T[dim 4dq+i][keys 4kq..4kq+3]
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int w = i >> 1;
-      const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;  // high or low halves
-      u32x2 out;
-      out[0] = __builtin_amdgcn_perm(vr[u][1][w], vr[u][0][w], sel);
-      out[1] = __builtin_amdgcn_perm(vr[u][3][w], vr[u][2][w], sel);
-      *reinterpret_cast<u32x2*>(vt + ((4 * dq + i) * VP + 4 * kq) * 2) = out;
-    }
+  for (int i = 0; i < NI; ++i) {
+    const int r0 = 8 * (w + kWaves * i);
+    if (r0 >= rpad) break;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(Ks + r0 * 128),
+                                             16, off[i], 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(Vs + r0 * 128),
+                                             16, off[i], 0, 0, 0);
   }
 }
 
 // One sequence (image or packed run), one head.  rq/rk/rv/ro cover the
 // sequence's head slice; roff(r) is the byte offset of its row r.
-template <int DT, typename RowOff>
+// `last_use()` is called by every thread once, right after the sequence's
+// kept-row list (through roff) has been read for the last time: at the last
+// chunk of the last pass, before its multiply.
+template <int DT, typename RowOff, typename Hook>
 __device__ __forceinline__ void attend_seq16(const AttnParams& p, int n, unsigned char* kvbase,
-                                             Rsrc rq, Rsrc rk, Rsrc rv, Rsrc ro, RowOff roff) {
+                                             Rsrc rq, Rsrc rk, Rsrc rv, Rsrc ro, RowOff roff,
+                                             Hook last_use) {
   typedef Half16<DT> Tr;
   typedef typename Tr::T T;
   typedef typename Tr::V8 V8;
   typedef typename Tr::V4 V4;
   const int lane = lane_id(), w = wave_id(), g = lane >> 4, r16 = lane & 15;
-  const int kc = p.kc, VP = kc + kVPad16;
-  T* Ks = reinterpret_cast<T*>(kvbase);
-  T* Vt = Ks + kc * kHeadDim;
+  const int kc = p.kc;
+  unsigned char* Ks = kvbase;
+  unsigned char* Vs = kvbase + kc * kHeadDim * 2;
   constexpr int kWaves = kAttnThreads16 / 64;
   constexpr int kPerPass = kWaves * kQBlocksPerWave;
   const int nqb = (n + kQBlock - 1) / kQBlock;
@@ -321,9 +313,10 @@ __device__ __forceinline__ void attend_seq16(const AttnParams& p, int n, unsigne
       const int rows = min(kc, n - c0);
       if (!(pass > 0 && cc == 0)) {
         if (pass > 0 || cc > 0) __syncthreads();
-        stage16<DT>(rk, rv, Ks, Vt, VP, c0, rows, roff);
+        stage16<DT>(rk, rv, Ks, Vs, c0, rows, roff);
         __syncthreads();
       }
+      if (pass == npass - 1 && cc == nchunk - 1) last_use();
       if (cc == 0) {  // accumulators come alive only after the first staging
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
@@ -336,7 +329,7 @@ __device__ __forceinline__ void attend_seq16(const AttnParams& p, int n, unsigne
         const int ntile = (rows + kKeyTile - 1) / kKeyTile;
         for (int t = 0; t < ntile; ++t) {
           const int k0 = t * kKeyTile;
-          tile16<DT>(Ks, Vt, VP, k0, min(kKeyTile, rows - k0), qf, o, m, act[1], c);
+          tile16<DT>(Ks, Vs, k0, min(kKeyTile, rows - k0), qf, o, m, act[1], c);
         }
       }
     }
@@ -569,7 +562,7 @@ __device__ __forceinline__ void attend_body(const AttnParams& p, unsigned char* 
       const uint32_t bytes = (uint32_t)N * rs * ES;
       auto roff = [=](int r) -> uint32_t { return (uint32_t)idx[min(r, n - 1)] * (rs * ES); };
       attend_seq16<DT>(pl, n, kvbase, make_rsrc(pl.q, bytes), make_rsrc(pl.k, bytes),
-                       make_rsrc(pl.v, bytes), make_rsrc(pl.o, bytes), roff);
+                       make_rsrc(pl.v, bytes), make_rsrc(pl.o, bytes), roff, [] {});
     }
   } else {
     const int row0 = p.cu[b];
@@ -583,7 +576,7 @@ __device__ __forceinline__ void attend_body(const AttnParams& p, unsigned char* 
       const uint32_t bytes = (uint32_t)n * rs * ES;
       auto roff = [=](int r) -> uint32_t { return (uint32_t)r * (rs * ES); };
       attend_seq16<DT>(pl, n, smem, make_rsrc(pl.q, bytes), make_rsrc(pl.k, bytes),
-                       make_rsrc(pl.v, bytes), make_rsrc(pl.o, bytes), roff);
+                       make_rsrc(pl.v, bytes), make_rsrc(pl.o, bytes), roff, [] {});
     }
   }
 }
@@ -601,11 +594,155 @@ __global__ __launch_bounds__(kAttnThreads32) void attend32_kernel(AttnParams p) 
   attend_body<0, FUSED>(p, smem);
 }
 
-static hipError_t set_lds_limit(const void* fn) {
-  return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+// Persistent form of the fused 16-bit kernel.  A grid of resident
+// workgroups pulls (image, head) items from a device counter instead of
+// being dispatched one item each.  That removes the dispatch gap between
+// items, and it takes the mask round trip off the critical path: while item
+// i runs, the workgroup already holds the index of item i + 1 (fetched one
+// item ahead), pulls its mask row into LDS with direct-to-LDS loads, and
+// compacts it as soon as item i no longer reads its own kept-row list
+// (before item i's multiply).  At the item boundary the next item's loads
+// issue at once.  The workgroup that leaves last returns the counter to
+// zero for the next launch.
+// A workgroup barrier that orders LDS only: this wave's LDS accesses
+// complete, then s_barrier; no wait for global memory.  The clobber keeps the
+// compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+constexpr int kMaskWindow = 2048;  // LDS bytes for one mask row (N + 3 <= 1027, whole dwords)
+constexpr int kPersistentStaticLds = kMaskWindow + 256;
+
+template <int DT>
+__global__ __launch_bounds__(kAttnThreads16, 3) void attend16_persistent_kernel(AttnParams p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ __align__(16) unsigned char s_mask[kMaskWindow];  // its own LDS object, see below
+  __shared__ int s_item;
+  constexpr int NT = kAttnThreads16;
+  constexpr int PER = compact_per<NT>();
+  constexpr int ES = 2;
+  const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
+  const int H = p.H, N = p.N, G = p.B * p.H;
+  if (blockIdx.x == 0 && (p.cu_out || p.max_out)) {
+    count_scan_block<NT>(p.mask, p.B, N, p.cu_out, p.max_out, reinterpret_cast<int*>(smem));
+    __syncthreads();
+  }
+  const uint32_t mask_bytes = (uint32_t)p.B * (uint32_t)N;
+  const uint32_t mask_tail = mask_bytes & ~3u;  // bytes at or past it are read directly
+  const Rsrc rmask = make_rsrc(p.mask, mask_bytes);
+  // The mask row of `item` as whole dwords into s_mask (lane L of a load
+  // lands at byte 4 L).  s_mask is a separate LDS object so that the
+  // compiler's wait for these loads is not attached to reads of smem.
+  auto prefetch_mask = [&](int item) {
+    const uint32_t a0 = ((uint32_t)(item / H) * (uint32_t)N) & ~3u;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int dw0 = u * 256 + w * 64;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rmask, (__attribute__((address_space(3))) void*)(s_mask + dw0 * 4), 4,
+          a0 + (uint32_t)(dw0 + lane) * 4, 0, 0, 0);
+    }
+  };
+  int32_t* idx = reinterpret_cast<int32_t*>(smem);
+  const size_t off = (size_t)round_up(N * 4, 16);
+  uint64_t* ballots = reinterpret_cast<uint64_t*>(smem + off);
+  int32_t* cnt = reinterpret_cast<int32_t*>(smem + off + 16 * 8);
+  unsigned char* kvbase = smem + attn_compact_bytes(N);
+  // compaction of `item` from the prefetched row (its last bytes past the
+  // final whole dword of the mask tensor straight from memory)
+  auto compact_item = [&](int item) -> int {
+    const uint32_t start = (uint32_t)(item / H) * (uint32_t)N;
+    const unsigned char* row = s_mask + (start & 3u);
+    uint8_t mb[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int j = (w + i * (NT / 64)) * 64 + lane;
+      mb[i] = 0;
+      if (j < N) mb[i] = start + (uint32_t)j < mask_tail ? row[j] : p.mask[start + j];
+    }
+    return compact_bytes<NT>(mb, N, idx, nullptr, ballots, cnt);
+  };
+
+  if (tid == 0) s_item = atomicAdd(p.work, 1);
+  __syncthreads();
+  int cur = s_item;
+  __syncthreads();
+  if (tid == 0) s_item = atomicAdd(p.work, 1);
+  if (cur < G) prefetch_mask(cur);
+  __syncthreads();  // (with its fence: the fetch and the prefetch have landed)
+  int nxt = s_item;
+  int n = cur < G ? compact_item(cur) : 0;
+  const uint32_t rs = (uint32_t)(H * kHeadDim);
+  while (cur < G) {
+    int pending = G;  // thread 0: index of the item after nxt
+    if (tid == 0 && nxt < G) pending = atomicAdd(p.work, 1);
+    if (nxt < G) prefetch_mask(nxt);
+    int n_next = 0;
+    // runs once all of cur's kept-row reads are done; the fetch and the
+    // prefetch were issued before cur's first staging, whose barrier (with
+    // its memory fence) has already seen them land
+    auto next_ready = [&] {
+      if (tid == 0) s_item = pending;
+      n_next = nxt < G ? compact_item(nxt) : 0;
+    };
+    const int b = cur / H, h = cur - b * H;
+    const AttnParams pl = rebase(p, ((size_t)b * N * H + h) * kHeadDim, ES);
+    zero_pruned<NT, ES>(static_cast<char*>(pl.o), ballots, N, H);
+    if (n > 0) {
+      const uint32_t bytes = (uint32_t)N * rs * ES;
+      auto roff = [=](int r) -> uint32_t { return (uint32_t)idx[min(r, n - 1)] * (rs * ES); };
+      attend_seq16<DT>(pl, n, kvbase, make_rsrc(pl.q, bytes), make_rsrc(pl.k, bytes),
+                       make_rsrc(pl.v, bytes), make_rsrc(pl.o, bytes), roff, next_ready);
+    } else {
+      __syncthreads();  // every wave's zero fill read the ballots; fetch and prefetch landed
+      next_ready();
+    }
+    // Item boundary: only LDS is shared across it (cur's staged rows, s_item),
+    // so the barriers wait for this wave's LDS accesses but not, as
+    // __syncthreads would, for cur's output stores still draining.
+    lds_barrier();  // every wave is done with cur's LDS and has written s_item
+    cur = nxt;
+    nxt = s_item;
+    n = n_next;
+    lds_barrier();  // s_item is read before the next iteration writes it
+  }
+  if (tid == 0) {
+    __threadfence();
+    if (atomicAdd(p.work + 1, 1) == (int)gridDim.x - 1) {
+      atomicExch(p.work, 0);
+      atomicExch(p.work + 1, 0);
+    }
+  }
+}
+
+int attend_persistent_per_cu(int N, int kc) {
+  const size_t lds = attn_lds_bytes(1, true, N, kc) + kPersistentStaticLds;
+  const int by_lds = (int)((160 * 1024) / lds);
+  return by_lds < 3 ? by_lds : 3;  // 3 waves per SIMD by registers
+}
+
+hipError_t launch_attend_persistent(const AttnParams& p, int dtype, int grid, hipStream_t s) {
+  const size_t lds = attn_lds_bytes(dtype, true, p.N, p.kc);
+  if (dtype == 1)
+    hipLaunchKernelGGL((attend16_persistent_kernel<1>), dim3(grid), dim3(kAttnThreads16), lds, s, p);
+  else
+    hipLaunchKernelGGL((attend16_persistent_kernel<2>), dim3(grid), dim3(kAttnThreads16), lds, s, p);
+  return hipGetLastError();
+}
+
+// Dynamic LDS limit: the 160 KB of a CU minus the kernel's static LDS.
+static hipError_t set_lds_limit(const void* fn, int static_bytes = 0) {
+  return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                             160 * 1024 - static_bytes);
 }
 
 hipError_t attend_init() {
+  for (const void* f : {reinterpret_cast<const void*>(&attend16_persistent_kernel<1>),
+                        reinterpret_cast<const void*>(&attend16_persistent_kernel<2>)}) {
+    hipError_t e = set_lds_limit(f, kPersistentStaticLds);
+    if (e != hipSuccess) return e;
+  }
   const void* fns[6] = {reinterpret_cast<const void*>(&attend32_kernel<false>),
                         reinterpret_cast<const void*>(&attend32_kernel<true>),
                         reinterpret_cast<const void*>(&attend16_kernel<1, false>),

@@ -186,18 +186,37 @@ __device__ __forceinline__ void count_scan_block(const uint8_t* __restrict__ mas
   if (tid == 0 && max_out) *max_out = mx;
 }
 
-// Row compaction: for one image's mask row (N <= 1024 bytes) build the
-// ascending list of kept positions idx[0..n) in LDS and return n (the same
-// value in every thread).  Each wave takes 64-token chunks; a ballot gives
-// every kept lane its rank inside the chunk, a prefix over the (at most 16)
-// chunk counts gives the chunk's base.  Optionally stores rank[j] (-1 for a
-// pruned token) and the per-chunk ballots.  `cnt` holds 16 ints.  Contains
-// two barriers; every thread must call it.
+// Mask bytes a thread contributes to the row compaction below: chunk
+// c = wave + i * waves, token j = 64 c + lane, zero past N.  Loading them is
+// the compaction's only global access, so a caller can issue it early.
 template <int NT>
-__device__ int compact_row(const uint8_t* __restrict__ mrow, int N, int32_t* idx, int32_t* rank,
-                           uint64_t* ballots, int32_t* cnt) {
+constexpr int compact_per() { return (16 + NT / 64 - 1) / (NT / 64); }
+
+template <int NT>
+__device__ __forceinline__ void mask_row_bytes(const uint8_t* __restrict__ mrow, int N,
+                                               uint8_t (&mb)[compact_per<NT>()]) {
   constexpr int W = NT / 64;
-  constexpr int PER = (16 + W - 1) / W;  // chunks per wave (N <= 1024)
+  const int lane = lane_id(), w = wave_id();
+#pragma unroll
+  for (int i = 0; i < compact_per<NT>(); ++i) {
+    const int j = (w + i * W) * 64 + lane;
+    mb[i] = j < N ? mrow[j] : (uint8_t)0;
+  }
+}
+
+// Row compaction: for one image's mask row (N <= 1024 bytes, given as the
+// bytes of mask_row_bytes) build the ascending list of kept positions
+// idx[0..n) in LDS and return n (the same value in every thread).  Each wave
+// takes 64-token chunks; a ballot gives every kept lane its rank inside the
+// chunk, a prefix over the (at most 16) chunk counts gives the chunk's base.
+// Optionally stores rank[j] (-1 for a pruned token) and the per-chunk
+// ballots.  `cnt` holds 16 ints.  Contains two barriers; every thread must
+// call it.
+template <int NT>
+__device__ int compact_bytes(const uint8_t (&mb)[compact_per<NT>()], int N, int32_t* idx,
+                             int32_t* rank, uint64_t* ballots, int32_t* cnt) {
+  constexpr int W = NT / 64;
+  constexpr int PER = compact_per<NT>();
   const int lane = lane_id(), w = wave_id();
   const int nchunks = (N + 63) >> 6;
   uint64_t bal[PER];
@@ -205,8 +224,7 @@ __device__ int compact_row(const uint8_t* __restrict__ mrow, int N, int32_t* idx
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int c = w + i * W;
-    const int j = c * 64 + lane;
-    keep[i] = (c < nchunks) && (j < N) && (mrow[j] != 0);
+    keep[i] = (c < nchunks) && (mb[i] != 0);
     bal[i] = __ballot(keep[i]);
     if (c < nchunks && lane == 0) {
       cnt[c] = __popcll(bal[i]);
@@ -230,6 +248,14 @@ __device__ int compact_row(const uint8_t* __restrict__ mrow, int N, int32_t* idx
   }
   __syncthreads();
   return n;
+}
+
+template <int NT>
+__device__ int compact_row(const uint8_t* __restrict__ mrow, int N, int32_t* idx, int32_t* rank,
+                           uint64_t* ballots, int32_t* cnt) {
+  uint8_t mb[compact_per<NT>()];
+  mask_row_bytes<NT>(mrow, N, mb);
+  return compact_bytes<NT>(mb, N, idx, rank, ballots, cnt);
 }
 
 }  // namespace rva

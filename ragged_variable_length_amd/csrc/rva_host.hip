@@ -355,6 +355,37 @@ int enqueue_linear(const rva::LinearParams& p, int dtype, hipStream_t s) {
   return RVA_OK;
 }
 
+// Compute units of the current device (cached per device).
+int device_cus(int* out) {
+  static int cache[64] = {0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev >= 0 && dev < 64 && cache[dev] > 0) {
+    *out = cache[dev];
+    return RVA_OK;
+  }
+  int cus = 0;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail(e, "device attribute");
+  if (dev >= 0 && dev < 64) cache[dev] = cus;
+  *out = cus;
+  return RVA_OK;
+}
+
+int enqueue_attend_persistent(const rva::AttnParams& p, int dtype, hipStream_t s) {
+  RVA_TRY(ensure_init());
+  int cus = 0;
+  RVA_TRY(device_cus(&cus));
+  const long long items = (long long)p.B * p.H;
+  long long grid = (long long)rva::attend_persistent_per_cu(p.N, p.kc) * cus;
+  if (grid > items) grid = items;
+  if (grid < 1) grid = 1;
+  hipError_t e = rva::launch_attend_persistent(p, dtype, (int)grid, s);
+  if (e != hipSuccess) return hip_fail(e, "persistent launch");
+  return RVA_OK;
+}
+
 int enqueue_attend(const rva::AttnParams& p, int dtype, bool fused, hipStream_t s) {
   RVA_TRY(ensure_init());
   hipError_t e = rva::launch_attend(p, dtype, fused, s);
@@ -367,6 +398,7 @@ int enqueue_attend(const rva::AttnParams& p, int dtype, bool fused, hipStream_t 
 struct rva_plan_s {
   hipGraph_t graph;
   hipGraphExec_t exec;
+  int32_t* work;  // persistent mode: the plan's own work counter (device), else NULL
 };
 
 namespace {
@@ -398,7 +430,7 @@ int capture_plan(rva_plan* out, F enqueue) {
     (void)hipGraphDestroy(graph);
     return hip_fail(e, "graph instantiate");
   }
-  rva_plan_s* plan = new (std::nothrow) rva_plan_s{graph, exec};
+  rva_plan_s* plan = new (std::nothrow) rva_plan_s{graph, exec, nullptr};
   if (!plan) {
     (void)hipGraphExecDestroy(exec);
     (void)hipGraphDestroy(graph);
@@ -412,7 +444,7 @@ int capture_plan(rva_plan* out, F enqueue) {
 
 extern "C" {
 
-int rva_version(void) { return 103; }
+int rva_version(void) { return 104; }
 
 const char* rva_status_string(int status) {
   switch (status) {
@@ -485,6 +517,20 @@ int rva_out_projection(const void* o, const int32_t* kept_index, const int32_t* 
   return enqueue_linear(p, dtype, static_cast<hipStream_t>(stream));
 }
 
+int rva_fused_persistent(const void* q_pad, const void* k_pad, const void* v_pad,
+                         const uint8_t* mask, int B, int N, int H, int d, int max_seqlen_hint,
+                         float softmax_scale, int dtype, void* o_pad, int32_t* cu_seqlens,
+                         int32_t* max_seqlen, int32_t* work, void* stream) {
+  rva::AttnParams p;
+  RVA_TRY(validate_fused(q_pad, k_pad, v_pad, mask, B, N, H, d, max_seqlen_hint, softmax_scale,
+                         dtype, o_pad, cu_seqlens, max_seqlen, &p));
+  RVA_TRY(check_i32(work, "work", true));
+  if (dtype == RVA_F32)  // the persistent form is built for 16-bit inputs; fp32 keeps one launch
+    return enqueue_attend(p, dtype, true, static_cast<hipStream_t>(stream));
+  p.work = work;
+  return enqueue_attend_persistent(p, dtype, static_cast<hipStream_t>(stream));
+}
+
 int rva_empty(int count, void* stream) {
   if (count < 0) return fail(RVA_ERR_INVALID, "count must be >= 0");
   for (int i = 0; i < count; ++i) {
@@ -519,6 +565,11 @@ int rva_plan_create(const rva_plan_desc* desc, rva_plan* out) {
                              D.max_seqlen_hint, D.softmax_scale, D.dtype, D.o_pad, D.cu_seqlens,
                              D.max_seqlen, &attn));
       break;
+    case RVA_PLAN_PERSISTENT:
+      RVA_TRY(validate_fused(D.q_pad, D.k_pad, D.v_pad, D.mask, D.B, D.N, D.H, D.d,
+                             D.max_seqlen_hint, D.softmax_scale, D.dtype, D.o_pad, D.cu_seqlens,
+                             D.max_seqlen, &attn));
+      break;
     case RVA_PLAN_L2_FUSED:
       RVA_TRY(validate_threshold(D.x, D.B, D.N, D.C, D.x_dtype, D.keep_quantile, D.mask_out,
                                  &thr));
@@ -532,7 +583,18 @@ int rva_plan_create(const rva_plan_desc* desc, rva_plan* out) {
       return fail(RVA_ERR_INVALID, "unknown plan mode %d", D.mode);
   }
   RVA_TRY(ensure_init());
-  return capture_plan(out, [&](hipStream_t cs) -> int {
+  // persistent mode owns a zeroed two-int work counter for its whole life
+  int32_t* work = nullptr;
+  if (D.mode == RVA_PLAN_PERSISTENT) {
+    hipError_t e = hipMalloc(&work, 2 * sizeof(int32_t));
+    if (e != hipSuccess) return hip_fail(e, "work counter allocation");
+    e = hipMemset(work, 0, 2 * sizeof(int32_t));
+    if (e != hipSuccess) {
+      (void)hipFree(work);
+      return hip_fail(e, "work counter reset");
+    }
+  }
+  const int st0 = capture_plan(out, [&](hipStream_t cs) -> int {
     hipError_t e;
     int st = RVA_OK;
     switch (D.mode) {
@@ -547,6 +609,11 @@ int rva_plan_create(const rva_plan_desc* desc, rva_plan* out) {
     case RVA_PLAN_FUSED:
       st = enqueue_attend(attn, D.dtype, true, cs);
       break;
+    case RVA_PLAN_PERSISTENT:
+      attn.work = work;
+      st = D.dtype == RVA_F32 ? enqueue_attend(attn, D.dtype, true, cs)
+                              : enqueue_attend_persistent(attn, D.dtype, cs);
+      break;
     case RVA_PLAN_L2_FUSED:
       st = enqueue_threshold(thr, cs);
       if (st == RVA_OK) st = enqueue_attend(attn, D.dtype, true, cs);
@@ -558,6 +625,12 @@ int rva_plan_create(const rva_plan_desc* desc, rva_plan* out) {
     }
     return st;
   });
+  if (st0 != RVA_OK) {
+    if (work) (void)hipFree(work);
+    return st0;
+  }
+  (*out)->work = work;
+  return RVA_OK;
 }
 
 int rva_layers_plan_create(const rva_layers_desc* desc, rva_plan* out) {
@@ -613,6 +686,7 @@ int rva_plan_destroy(rva_plan plan) {
   if (!plan) return RVA_OK;
   (void)hipGraphExecDestroy(plan->exec);
   (void)hipGraphDestroy(plan->graph);
+  if (plan->work) (void)hipFree(plan->work);
   delete plan;
   return RVA_OK;
 }

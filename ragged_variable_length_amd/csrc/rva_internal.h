@@ -17,12 +17,10 @@ constexpr int kKeyTile = 32;        // keys per inner step
 constexpr int kPackThreads = 256;
 constexpr int kScanThreads = 1024;
 
-// Keys staged on chip per chunk.  16-bit: K rows [kc][64] halves (16-byte
-// pieces XOR-swizzled by row) + V^T [64][kc + 8] halves; fp32: K and V rows
-// [kc][68] floats.
+// Keys staged on chip per chunk.  16-bit: K and V rows [kc][64] halves each
+// (16-byte pieces XOR-swizzled by row); fp32: K and V rows [kc][68] floats.
 constexpr int kKcMax16 = 192;
 constexpr int kKcMax32 = 128;
-constexpr int kVPad16 = 8;     // halves of pad per staged V^T row
 constexpr int kPitch32 = 68;   // floats per staged K/V row for fp32
 
 struct AttnParams {
@@ -37,6 +35,7 @@ struct AttnParams {
   int B, N, H;
   int kc;                 // keys per staged chunk (multiple of kKeyTile)
   float scale_log2e;      // softmax scale * log2(e)
+  int32_t* work;          // persistent form: [next item, workgroups done], zero between launches
 };
 
 struct CopyParams {
@@ -86,8 +85,7 @@ __host__ __device__ inline size_t attn_compact_bytes(int N) {
 inline int attn_threads(int dtype) { return dtype == 0 ? kAttnThreads32 : kAttnThreads16; }
 
 inline size_t attn_lds_bytes(int dtype, bool fused, int N, int kc) {
-  size_t kv = dtype == 0 ? (size_t)kc * kPitch32 * 4 * 2
-                         : (size_t)kc * kHeadDim * 2 + (size_t)kHeadDim * (kc + kVPad16) * 2;
+  size_t kv = dtype == 0 ? (size_t)kc * kPitch32 * 4 * 2 : (size_t)kc * kHeadDim * 2 * 2;
   size_t head = fused ? attn_compact_bytes(N) : 0;
   size_t scan = (size_t)(4 * attn_threads(dtype) + 64) * 4;  // fused scan workgroup reuses LDS
   size_t total = head + kv;
@@ -100,6 +98,10 @@ hipError_t launch_count_scan(const uint8_t* mask, int B, int N, int32_t* cu, int
 hipError_t launch_pack(const CopyParams& p, int splits, hipStream_t s);
 hipError_t launch_unpack(const CopyParams& p, int splits, hipStream_t s);
 hipError_t launch_attend(const AttnParams& p, int dtype, bool fused, hipStream_t s);
+// Fused 16-bit path as a persistent grid of `grid` workgroups pulling
+// (image, head) items from p.work.
+hipError_t launch_attend_persistent(const AttnParams& p, int dtype, int grid, hipStream_t s);
+int attend_persistent_per_cu(int N, int kc);  // resident workgroups per CU
 hipError_t launch_empty(hipStream_t s);
 hipError_t attend_init();  // raises the dynamic-LDS limit of every attention kernel
 hipError_t launch_threshold(const ThreshParams& p, int B, int dtype, hipStream_t s);

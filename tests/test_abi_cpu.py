@@ -33,7 +33,8 @@ def test_header_lists_the_entry_points():
     for want in ("rva_pack", "rva_ragged_attend", "rva_unpack", "rva_fused", "rva_plan_create",
                  "rva_plan_launch", "rva_plan_destroy", "rva_empty", "rva_status_string",
                  "rva_last_error", "rva_version", "rva_threshold_l2_mask",
-                 "rva_qkv_projection", "rva_out_projection", "rva_layers_plan_create"):
+                 "rva_qkv_projection", "rva_out_projection", "rva_layers_plan_create",
+                 "rva_fused_persistent"):
         assert want in names
 
 
@@ -48,7 +49,7 @@ def test_status_strings(L):
     assert L.rva_status_string(-2) == b"unsupported configuration"
     assert L.rva_status_string(-3) == b"HIP runtime error"
     assert L.rva_status_string(99) == b"unknown status"
-    assert L.rva_version() == 103
+    assert L.rva_version() == 104
 
 
 FAKE = ctypes.c_void_p(0x7F0000000000)  # aligned, never dereferenced: validation fails first
@@ -84,6 +85,13 @@ def test_attend_unpack_fused_validation(L):
     assert L.rva_fused(FAKE, FAKE, FAKE, FAKE, 2, 8, 1, 64, 0, f, 1, FAKE,
                        ctypes.c_void_p(0x7F0000000002), None, None) == -1
     assert L.rva_empty(-1, None) == -1
+    # persistent form: the work counter is required and 4-byte aligned
+    assert L.rva_fused_persistent(FAKE, FAKE, FAKE, FAKE, 2, 8, 1, 64, 0, f, 1, FAKE, None, None,
+                                  None, None) == -1 and b"work" in L.rva_last_error()
+    assert L.rva_fused_persistent(FAKE, FAKE, FAKE, FAKE, 2, 8, 1, 64, 0, f, 1, FAKE, None, None,
+                                  ctypes.c_void_p(0x7F0000000002), None) == -1
+    assert L.rva_fused_persistent(FAKE, FAKE, FAKE, None, 2, 8, 1, 64, 0, f, 1, FAKE, None, None,
+                                  FAKE, None) == -1 and b"mask" in L.rva_last_error()
 
 
 def test_threshold_validation(L):

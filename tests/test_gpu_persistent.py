@@ -1,0 +1,120 @@
+"""The persistent form of the fused path: identical bits to the one-launch
+fused kernel (same per-item code), the oracle on the standard workloads, the
+work counter back at zero after every call, and the persistent plan's
+replays."""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+from gpu_util import TOL, bits, f64, max_err, upload  # noqa: E402
+
+
+def _rva():
+    import ragged_variable_length_amd as rva
+    rva.lib()
+    return rva
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _outs(q, device):
+    B = q.shape[0]
+    return (torch.empty_like(q), torch.empty(B + 1, dtype=torch.int32, device=device),
+            torch.empty(1, dtype=torch.int32, device=device))
+
+
+WORKLOADS = [("deit_s", lambda: W.deit_s_224_threshold_l2()),
+             ("deit_b_p50", lambda: W.deit_b_224(0.5)),
+             ("deit_b_p0", lambda: W.deit_b_224(0.0)),
+             ("deit_b_384", lambda: W.deit_b_384()),
+             ("tiny_counts", lambda: W.random_workload(seed=5, B=3, N=40, H=2, dtype="bf16",
+                                                        counts=[40, 0, 1]))]
+
+
+@pytest.mark.parametrize("name,make", WORKLOADS, ids=[n for n, _ in WORKLOADS])
+def test_persistent_equals_fused_and_oracle(device, name, make):
+    rva = _rva()
+    w = make()
+    _say(f"[persistent] {name}")
+    q, k, v, mask = upload(w, device)
+    hint = int(w.counts.max()) if w.counts.max() > 0 else 1
+    work = torch.zeros(2, dtype=torch.int32, device=device)
+    o1, cu1, mx1 = _outs(q, device)
+    o2, cu2, mx2 = _outs(q, device)
+    rva.fused(q, k, v, mask, out=o1, cu_seqlens=cu1, max_seqlen=mx1, max_seqlen_hint=hint)
+    for _ in range(2):  # the second call checks the counter came back to zero
+        o2.fill_(7.0)
+        rva.fused_persistent(q, k, v, mask, work, out=o2, cu_seqlens=cu2, max_seqlen=mx2,
+                             max_seqlen_hint=hint)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(o2), bits(o1))
+        assert np.array_equal(cu2.cpu().numpy(), cu1.cpu().numpy())
+        assert int(mx2.item()) == int(mx1.item())
+        assert work.cpu().tolist() == [0, 0]
+    ref, cu_ref, mx_ref, _ = oracle.pack_attend_unpack(w.q, w.k, w.v, w.mask, w.dtype)
+    assert np.array_equal(cu2.cpu().numpy(), cu_ref)
+    assert max_err(f64(o2), ref) <= TOL[w.dtype]
+
+
+def test_persistent_fewer_items_than_workgroups(device):
+    """Two images of one head: most resident workgroups find no item."""
+    rva = _rva()
+    w = W.random_workload(seed=9, B=2, N=197, H=1, dtype="f16", counts=[197, 60])
+    q, k, v, mask = upload(w, device)
+    work = torch.zeros(2, dtype=torch.int32, device=device)
+    o = rva.fused_persistent(q, k, v, mask, work, max_seqlen_hint=197)
+    torch.cuda.synchronize()
+    ref, _, _, _ = oracle.pack_attend_unpack(w.q, w.k, w.v, w.mask, w.dtype)
+    assert max_err(f64(o), ref) <= TOL[w.dtype]
+    assert work.cpu().tolist() == [0, 0]
+
+
+def test_persistent_plan_replays(device):
+    rva = _rva()
+    w = W.deit_b_224(0.5)
+    q, k, v, mask = upload(w, device)
+    B, N, H, d = q.shape
+    out, cu, mx = _outs(q, device)
+    plan = rva.Plan(rva.PERSISTENT, q=q, k=k, v=v, mask=mask, out=out, cu_seqlens=cu,
+                    max_seqlen=mx, max_seqlen_hint=N)
+    rng = np.random.Generator(np.random.PCG64(44))
+    for rep in range(4):
+        m = w.mask if rep == 0 else (rng.random((B, N)) < rng.uniform(0.1, 0.9)).astype(np.uint8)
+        mask.copy_(torch.from_numpy(m))
+        plan.launch()
+        torch.cuda.synchronize()
+        ref_o = rva.fused(q, k, v, mask, max_seqlen_hint=N)  # eager work between replays
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(out), bits(ref_o)), rep
+        ref, cu_ref, _, _ = oracle.pack_attend_unpack(w.q, w.k, w.v, m, w.dtype)
+        assert np.array_equal(cu.cpu().numpy(), cu_ref)
+        assert max_err(f64(out), ref) <= TOL[w.dtype]
+    plan.close()
+
+
+def test_persistent_full_size(device):
+    """The mixed 1024-image batch: bits equal to the one-launch fused kernel."""
+    rva = _rva()
+    w = W.mixed_peak()
+    q, k, v, mask = upload(w, device)
+    work = torch.zeros(2, dtype=torch.int32, device=device)
+    o1, cu1, mx1 = _outs(q, device)
+    o2, cu2, mx2 = _outs(q, device)
+    rva.fused(q, k, v, mask, out=o1, cu_seqlens=cu1, max_seqlen=mx1, max_seqlen_hint=197)
+    for _ in range(3):
+        rva.fused_persistent(q, k, v, mask, work, out=o2, cu_seqlens=cu2, max_seqlen=mx2,
+                             max_seqlen_hint=197)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(o2), bits(o1))
+    assert np.array_equal(cu2.cpu().numpy(), cu1.cpu().numpy())
+    assert work.cpu().tolist() == [0, 0]
