@@ -5,7 +5,9 @@
 // image's kept tokens only, O = softmax(Q K^T * scale) V per image and head.
 //
 // Work decomposition (CDNA4 / gfx950), 16-bit inputs:
-//  * one workgroup of 4 waves per (image, head).  Post-pruning ViT sequences
+//  * one workgroup of 4 waves per (image, head); the fused form gives a
+//    workgroup two heads of one image in turn, so that its mask row is read
+//    and compacted once for both.  Post-pruning ViT sequences
 //    are short (at most 197 tokens at 224x224, 577 at 384x384), so the
 //    workgroup stages its sequence's K and V in LDS in one memory round trip,
 //    by direct-to-LDS loads; sequences longer than one chunk are staged in
@@ -541,7 +543,11 @@ __device__ __forceinline__ void attend_body(const AttnParams& p, unsigned char* 
       --bid;
     }
   }
-  const int b = bid / p.H, h = bid - b * p.H;
+  // fused 16-bit: a workgroup takes kFusedHeads heads of one image in turn,
+  // so the mask row is read and compacted once for all of them
+  constexpr int HG = (FUSED && DT != 0) ? kFusedHeads : 1;
+  const int ngrp = (p.H + HG - 1) / HG;
+  const int b = bid / ngrp, hg = bid - b * ngrp;
   const int H = p.H, N = p.N;
   constexpr int ES = DT == 0 ? 4 : 2;
   const uint32_t rs = (uint32_t)(H * kHeadDim);  // elements between consecutive token rows
@@ -551,20 +557,25 @@ __device__ __forceinline__ void attend_body(const AttnParams& p, unsigned char* 
     uint64_t* ballots = reinterpret_cast<uint64_t*>(smem + off);
     int32_t* cnt = reinterpret_cast<int32_t*>(smem + off + 16 * 8);
     const int n = compact_row<NT>(p.mask + (size_t)b * N, N, idx, nullptr, ballots, cnt);
-    const AttnParams pl = rebase(p, ((size_t)b * N * H + h) * kHeadDim, ES);
-    zero_pruned<NT, ES>(static_cast<char*>(pl.o), ballots, N, H);
-    if (n <= 0) return;
     unsigned char* kvbase = smem + attn_compact_bytes(N);
-    auto elem = [=](int r) -> uint32_t { return (uint32_t)idx[r] * rs; };
-    if constexpr (DT == 0) {
-      attend_seq32(pl, n, kvbase, elem);
-    } else {
-      const uint32_t bytes = (uint32_t)N * rs * ES;
-      auto roff = [=](int r) -> uint32_t { return (uint32_t)idx[min(r, n - 1)] * (rs * ES); };
-      attend_seq16<DT>(pl, n, kvbase, make_rsrc(pl.q, bytes), make_rsrc(pl.k, bytes),
-                       make_rsrc(pl.v, bytes), make_rsrc(pl.o, bytes), roff, [] {});
+    const int h1 = min(H, hg * HG + HG);
+    for (int h = hg * HG; h < h1; ++h) {
+      if (h > hg * HG) __syncthreads();  // the previous head's staged rows are consumed
+      const AttnParams pl = rebase(p, ((size_t)b * N * H + h) * kHeadDim, ES);
+      zero_pruned<NT, ES>(static_cast<char*>(pl.o), ballots, N, H);
+      if (n <= 0) continue;
+      auto elem = [=](int r) -> uint32_t { return (uint32_t)idx[r] * rs; };
+      if constexpr (DT == 0) {
+        attend_seq32(pl, n, kvbase, elem);
+      } else {
+        const uint32_t bytes = (uint32_t)N * rs * ES;
+        auto roff = [=](int r) -> uint32_t { return (uint32_t)idx[min(r, n - 1)] * (rs * ES); };
+        attend_seq16<DT>(pl, n, kvbase, make_rsrc(pl.q, bytes), make_rsrc(pl.k, bytes),
+                         make_rsrc(pl.v, bytes), make_rsrc(pl.o, bytes), roff, [] {});
+      }
     }
   } else {
+    const int h = hg;
     const int row0 = p.cu[b];
     const int n = p.cu[b + 1] - row0;
     if (n <= 0) return;
@@ -758,7 +769,8 @@ hipError_t attend_init() {
 
 hipError_t launch_attend(const AttnParams& p, int dtype, bool fused, hipStream_t s) {
   const size_t lds = attn_lds_bytes(dtype, fused, p.N, p.kc);
-  const int grid = p.B * p.H + ((fused && (p.cu_out || p.max_out)) ? 1 : 0);
+  const int hg = (fused && dtype != 0) ? kFusedHeads : 1;
+  const int grid = p.B * ((p.H + hg - 1) / hg) + ((fused && (p.cu_out || p.max_out)) ? 1 : 0);
   const dim3 blk(attn_threads(dtype));
   if (dtype == 0) {
     if (fused) hipLaunchKernelGGL((attend32_kernel<true>), dim3(grid), blk, lds, s, p);

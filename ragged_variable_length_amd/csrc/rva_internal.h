@@ -12,6 +12,7 @@ constexpr int kHeadDim = 64;
 constexpr int kAttnThreads16 = 256; // 4 waves per attention workgroup (16-bit inputs)
 constexpr int kAttnThreads32 = 512; // 8 waves per attention workgroup (fp32 inputs)
 constexpr int kQBlock = 16;         // query rows per matrix-core block
+constexpr int kFusedHeads = 2;      // heads per workgroup in the fused 16-bit kernel
 constexpr int kQBlocksPerWave = 2;  // query blocks a wave carries through one pass
 constexpr int kKeyTile = 32;        // keys per inner step
 constexpr int kPackThreads = 256;
