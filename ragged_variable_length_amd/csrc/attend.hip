@@ -5,9 +5,9 @@
 // image's kept tokens only, O = softmax(Q K^T * scale) V per image and head.
 //
 // Work decomposition (CDNA4 / gfx950), 16-bit inputs:
-//  * one workgroup of 4 waves per (image, head); the fused form gives a
-//    workgroup two heads of one image in turn, so that its mask row is read
-//    and compacted once for both.  Post-pruning ViT sequences
+//  * one workgroup of 4 waves per (image, head); on large batches the fused
+//    form gives a workgroup two heads of one image in turn, so that its mask
+//    row is read and compacted once for both.  Post-pruning ViT sequences
 //    are short (at most 197 tokens at 224x224, 577 at 384x384), so the
 //    workgroup stages its sequence's K and V in LDS in one memory round trip,
 //    by direct-to-LDS loads; sequences longer than one chunk are staged in
@@ -543,9 +543,9 @@ __device__ __forceinline__ void attend_body(const AttnParams& p, unsigned char* 
       --bid;
     }
   }
-  // fused 16-bit: a workgroup takes kFusedHeads heads of one image in turn,
-  // so the mask row is read and compacted once for all of them
-  constexpr int HG = (FUSED && DT != 0) ? kFusedHeads : 1;
+  // fused 16-bit: a workgroup may take several heads of one image in turn,
+  // so that the mask row is read and compacted once for all of them
+  const int HG = (FUSED && DT != 0) ? p.heads_per_wg : 1;
   const int ngrp = (p.H + HG - 1) / HG;
   const int b = bid / ngrp, hg = bid - b * ngrp;
   const int H = p.H, N = p.N;
@@ -769,7 +769,7 @@ hipError_t attend_init() {
 
 hipError_t launch_attend(const AttnParams& p, int dtype, bool fused, hipStream_t s) {
   const size_t lds = attn_lds_bytes(dtype, fused, p.N, p.kc);
-  const int hg = (fused && dtype != 0) ? kFusedHeads : 1;
+  const int hg = (fused && dtype != 0) ? p.heads_per_wg : 1;
   const int grid = p.B * ((p.H + hg - 1) / hg) + ((fused && (p.cu_out || p.max_out)) ? 1 : 0);
   const dim3 blk(attn_threads(dtype));
   if (dtype == 0) {

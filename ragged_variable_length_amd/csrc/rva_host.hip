@@ -386,8 +386,17 @@ int enqueue_attend_persistent(const rva::AttnParams& p, int dtype, hipStream_t s
   return RVA_OK;
 }
 
-int enqueue_attend(const rva::AttnParams& p, int dtype, bool fused, hipStream_t s) {
+int enqueue_attend(const rva::AttnParams& p0, int dtype, bool fused, hipStream_t s) {
   RVA_TRY(ensure_init());
+  rva::AttnParams p = p0;
+  p.heads_per_wg = 1;
+  if (fused && dtype != RVA_F32 && p.H > 1) {
+    // pair the heads of an image only when the pairs still fill every
+    // resident slot (3 per CU) at least twice over
+    int cus = 0;
+    RVA_TRY(device_cus(&cus));
+    if ((long long)p.B * ((p.H + 1) / 2) >= 2LL * 3 * cus) p.heads_per_wg = 2;
+  }
   hipError_t e = rva::launch_attend(p, dtype, fused, s);
   if (e != hipSuccess) return hip_fail(e, fused ? "fused launch" : "attention launch");
   return RVA_OK;

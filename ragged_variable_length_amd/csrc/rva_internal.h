@@ -12,7 +12,6 @@ constexpr int kHeadDim = 64;
 constexpr int kAttnThreads16 = 256; // 4 waves per attention workgroup (16-bit inputs)
 constexpr int kAttnThreads32 = 512; // 8 waves per attention workgroup (fp32 inputs)
 constexpr int kQBlock = 16;         // query rows per matrix-core block
-constexpr int kFusedHeads = 2;      // heads per workgroup in the fused 16-bit kernel
 constexpr int kQBlocksPerWave = 2;  // query blocks a wave carries through one pass
 constexpr int kKeyTile = 32;        // keys per inner step
 constexpr int kPackThreads = 256;
@@ -37,6 +36,7 @@ struct AttnParams {
   int kc;                 // keys per staged chunk (multiple of kKeyTile)
   float scale_log2e;      // softmax scale * log2(e)
   int32_t* work;          // persistent form: [next item, workgroups done], zero between launches
+  int heads_per_wg;       // fused 16-bit form: heads of one image a workgroup takes in turn (>= 1)
 };
 
 struct CopyParams {
