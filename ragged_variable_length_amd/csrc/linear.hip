@@ -72,8 +72,8 @@ __device__ __forceinline__ u32x2 pack4(float a, float b, float c, float d) {
 
 constexpr int kLinBM = 256;        // product rows per workgroup
 constexpr int kLinBN = 256;        // output columns per workgroup
-constexpr int kLinK = 64;          // K per stage
-constexpr int kLinStages = 2;      // LDS ring depth (2 or 3)
+constexpr int kLinK = 64;          // K per stage (32 or 64)
+constexpr int kLinStages = 2;      // LDS ring depth (2 to 4)
 constexpr int kLinWM = 4;          // waves along the rows
 constexpr int kLinWN = 4;          // waves along the columns
 constexpr int kLinWaves = kLinWM * kLinWN;
@@ -81,15 +81,20 @@ constexpr int kLinThreads = 64 * kLinWaves;
 constexpr int kLinTM = kLinBM / kLinWM;  // a wave's rows
 constexpr int kLinTN = kLinBN / kLinWN;  // a wave's columns
 constexpr int kLinZeroRows = 64;   // padded rows per zero-fill workgroup
-constexpr int kStageA = kLinBM * 128;  // bytes of one stage's input tile
-constexpr int kStageB = kLinBN * 128;  // bytes of one stage's weight tile
+constexpr int kLinPitch = kLinK * 2;         // bytes of one staged row
+constexpr int kLinPieces = kLinK / 8;        // 16-byte pieces per staged row
+constexpr int kLinRowsPerLoad = 64 / kLinPieces;  // rows one 1 KB load fills
+constexpr int kStageA = kLinBM * kLinPitch;  // bytes of one stage's input tile
+constexpr int kStageB = kLinBN * kLinPitch;  // bytes of one stage's weight tile
 constexpr int kStageBytes = kStageA + kStageB;
-constexpr int kDmaA = kLinBM / 8 / kLinWaves;  // 1 KB (8-row) loads per wave per stage
-constexpr int kDmaB = kLinBN / 8 / kLinWaves;
-static_assert(kDmaA * 8 * kLinWaves == kLinBM && kDmaB * 8 * kLinWaves == kLinBN, "whole loads");
+constexpr int kDmaA = kLinBM / kLinRowsPerLoad / kLinWaves;  // 1 KB loads per wave per stage
+constexpr int kDmaB = kLinBN / kLinRowsPerLoad / kLinWaves;
+static_assert(kLinK == 32 || kLinK == 64, "K per stage");
+static_assert(kDmaA * kLinRowsPerLoad * kLinWaves == kLinBM &&
+              kDmaB * kLinRowsPerLoad * kLinWaves == kLinBN, "whole loads");
 constexpr int kDmaPerStage = kDmaA + kDmaB;  // vector memory ops per lane per stage
-static_assert(kDmaPerStage * 2 < 64, "two stages in flight must fit the wait counter");
-static_assert(kLinStages == 2 || kLinStages == 3, "ring depth");
+static_assert(kLinStages >= 2 && kLinStages <= 4, "ring depth");
+static_assert(kDmaPerStage * (kLinStages - 1) < 64, "stages in flight must fit the wait counter");
 
 constexpr int kLinGroupRows = 2;   // row blocks per XCD group
 
@@ -102,11 +107,14 @@ __host__ __device__ inline int linear_tile_slots(int m_tiles, int n_tiles) {
 
 typedef __attribute__((address_space(3))) void* LdsPtr;
 
-// Swizzle key of row r: piece p of the row is stored at slot p ^ key(r).
-__device__ __forceinline__ int lin_key(int r) { return r & 7; }
+// Swizzle key of row r: piece p of the row is stored at slot p ^ key(r).  For
+// 64-element rows the key is r mod 8; for 32-element rows (four pieces, four
+// rows per 256 bytes of banks) it is (r / 4) mod 4, so the 16 rows of a
+// 16-lane operand read hit 16 distinct bank groups.
+__device__ __forceinline__ int lin_key(int r) { return kLinK == 64 ? (r & 7) : ((r >> 2) & 3); }
 
-// byte offset of 16-byte piece p of row r in a [rows][64] half tile
-__device__ __forceinline__ int lin_swz(int r, int p) { return r * 128 + ((p ^ lin_key(r)) << 4); }
+// byte offset of 16-byte piece p of row r in a staged [rows][kLinK] half tile
+__device__ __forceinline__ int lin_swz(int r, int p) { return r * kLinPitch + ((p ^ lin_key(r)) << 4); }
 
 // Wait until at most N vector memory operations of this wave are in flight.
 template <int N>
@@ -125,7 +133,7 @@ __device__ __forceinline__ void bar() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_
 template <int DT>
 __device__ __forceinline__ void linear_tile(const LinearParams& p, int mb, int nb, int M,
                                             unsigned char* buf0, unsigned char* buf1,
-                                            unsigned char* buf2) {
+                                            unsigned char* buf2, unsigned char* buf3) {
   const int lane = lane_id(), w = wave_id();
   const int g = lane >> 4, r16 = lane & 15;
   const int wm = w / kLinWN, wn = w - wm * kLinWN;  // wave's kLinTM x kLinTN sub-tile
@@ -134,25 +142,26 @@ __device__ __forceinline__ void linear_tile(const LinearParams& p, int mb, int n
   const Rsrc rx = make_rsrc(p.x, (uint32_t)p.x_rows * kbytes);
   const Rsrc rw = make_rsrc(p.w, (uint32_t)p.Nout * kbytes);
 
-  // Direct-to-LDS loads: one instruction fills 8 rows (1 KB) of a stage, lane
-  // L landing at byte 16 L, i.e. row L / 8, slot L % 8.  The lane fetches the
-  // piece that belongs in that slot under the row swizzle, so LDS ends up in
-  // lin_swz order.  Rows past the product (or the weight) read out of range.
+  // Direct-to-LDS loads: one instruction fills kLinRowsPerLoad rows (1 KB) of a
+  // stage, lane L landing at byte 16 L, i.e. row L / kLinPieces, slot
+  // L % kLinPieces.  The lane fetches the piece that belongs in that slot
+  // under the row swizzle, so LDS ends up in lin_swz order.  Rows past the
+  // product (or the weight) read out of range.
   const int nkt = p.K / kLinK;
   uint32_t avoff[kDmaA], bvoff[kDmaB];
 #pragma unroll
   for (int i = 0; i < kDmaA; ++i) {
-    const int r = w * (kLinBM / kLinWaves) + 8 * i + (lane >> 3);  // tile row
+    const int r = w * (kLinBM / kLinWaves) + kLinRowsPerLoad * i + lane / kLinPieces;  // tile row
     const int m = m0 + r;
     int src = -1;
     if (m < M) src = p.x_index ? p.x_index[m] : m;
-    avoff[i] = src >= 0 ? (uint32_t)src * kbytes + (((lane & 7) ^ lin_key(r)) << 4) : kOOB;
+    avoff[i] = src >= 0 ? (uint32_t)src * kbytes + (((lane % kLinPieces) ^ lin_key(r)) << 4) : kOOB;
   }
 #pragma unroll
   for (int i = 0; i < kDmaB; ++i) {
-    const int r = w * (kLinBN / kLinWaves) + 8 * i + (lane >> 3);
+    const int r = w * (kLinBN / kLinWaves) + kLinRowsPerLoad * i + lane / kLinPieces;
     const int n = n0 + r;
-    bvoff[i] = n < p.Nout ? (uint32_t)n * kbytes + (((lane & 7) ^ lin_key(r)) << 4) : kOOB;
+    bvoff[i] = n < p.Nout ? (uint32_t)n * kbytes + (((lane % kLinPieces) ^ lin_key(r)) << 4) : kOOB;
   }
   // Stages past the last one are issued anyway (so that every step has the
   // same loads in flight and the wait counts stay static) through empty
@@ -161,15 +170,17 @@ __device__ __forceinline__ void linear_tile(const LinearParams& p, int mb, int n
   auto dma = [&](unsigned char* buf, int kt) {
     const bool live = kt < nkt;
     const Rsrc ra = live ? rx : rnone, rb = live ? rw : rnone;
-    const int koff = live ? kt * (kLinK * 2) : 0;
+    const int koff = live ? kt * kLinPitch : 0;
 #pragma unroll
     for (int i = 0; i < kDmaA; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          ra, (LdsPtr)(buf + (w * (kLinBM / kLinWaves) + 8 * i) * 128), 16, avoff[i], koff, 0, 0);
+          ra, (LdsPtr)(buf + (w * (kLinBM / kLinWaves) + kLinRowsPerLoad * i) * kLinPitch), 16,
+          avoff[i], koff, 0, 0);
 #pragma unroll
     for (int i = 0; i < kDmaB; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rb, (LdsPtr)(buf + kStageA + (w * (kLinBN / kLinWaves) + 8 * i) * 128), 16, bvoff[i], koff, 0, 0);
+          rb, (LdsPtr)(buf + kStageA + (w * (kLinBN / kLinWaves) + kLinRowsPerLoad * i) * kLinPitch),
+          16, bvoff[i], koff, 0, 0);
   };
 
   constexpr int NI = kLinTN / 16, NJ = kLinTM / 16;  // 16x16 blocks of a wave
@@ -183,7 +194,7 @@ __device__ __forceinline__ void linear_tile(const LinearParams& p, int mb, int n
     const unsigned char* As = buf;
     const unsigned char* Ws = buf + kStageA;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int ks = 0; ks < kLinK / 32; ++ks) {
       u32x4 wf[NI];
 #pragma unroll
       for (int i = 0; i < NI; ++i)
@@ -197,39 +208,23 @@ __device__ __forceinline__ void linear_tile(const LinearParams& p, int mb, int n
     }
   };
 
-  // Three-stage ring, two stages in flight.  Step kt: wait for this wave's
-  // loads of stage kt, barrier (every wave's loads of kt have landed and
-  // every wave is done with stage kt - 1), refill the stage-(kt - 1) buffer
-  // with stage kt + 2, multiply stage kt.  The ring is unrolled so that each
+  // Ring of kLinStages buffers, kLinStages - 1 stages in flight.  Step kt:
+  // wait for this wave's loads of stage kt (later stages may still be in
+  // flight), barrier (every wave's loads of stage kt have landed, every wave
+  // is done with stage kt - 1), refill stage kt - 1's buffer with stage
+  // kt + kLinStages - 1, multiply stage kt.  The ring is unrolled so that each
   // buffer is a distinct LDS object.
-  if constexpr (kLinStages == 3) {
-    auto step = [&](int kt, unsigned char* cur, unsigned char* refill) {
-      wait_vm<kDmaPerStage>();  // stage kt landed; stage kt + 1 may still be in flight
+  unsigned char* bufs[4] = {buf0, buf1, buf2, buf3};
+#pragma unroll
+  for (int st = 0; st < kLinStages - 1; ++st) dma(bufs[st], st);
+  for (int kt0 = 0; kt0 < nkt; kt0 += kLinStages) {
+#pragma unroll
+    for (int j = 0; j < kLinStages; ++j) {
+      const int kt = kt0 + j;
+      wait_vm<(kLinStages - 2) * kDmaPerStage>();
       bar();
-      dma(refill, kt + 2);
-      if (kt < nkt) compute(cur);
-    };
-    dma(buf0, 0);
-    dma(buf1, 1);
-    for (int kt = 0; kt < nkt; kt += 3) {
-      step(kt, buf0, buf2);
-      step(kt + 1, buf1, buf0);
-      step(kt + 2, buf2, buf1);
-    }
-  } else {
-    // two buffers, one stage in flight: wait for stage kt, barrier (every wave
-    // is done with stage kt - 1), refill its buffer with stage kt + 1, multiply
-    auto step = [&](int kt, unsigned char* cur, unsigned char* refill) {
-      wait_vm<0>();
-      bar();
-      dma(refill, kt + 1);
-      if (kt < nkt) compute(cur);
-    };
-    (void)buf2;
-    dma(buf0, 0);
-    for (int kt = 0; kt < nkt; kt += 2) {
-      step(kt, buf0, buf1);
-      step(kt + 1, buf1, buf0);
+      dma(bufs[(j + kLinStages - 1) % kLinStages], kt + kLinStages - 1);
+      if (kt < nkt) compute(bufs[j]);
     }
   }
   wait_vm<0>();
@@ -285,7 +280,8 @@ template <int DT>
 __global__ __launch_bounds__(kLinThreads, 1) void linear_kernel(LinearParams p) {
   __shared__ __align__(1024) unsigned char buf0[kStageBytes];
   __shared__ __align__(1024) unsigned char buf1[kStageBytes];
-  __shared__ __align__(1024) unsigned char buf2[kLinStages == 3 ? kStageBytes : 16];
+  __shared__ __align__(1024) unsigned char buf2[kLinStages >= 3 ? kStageBytes : 16];
+  __shared__ __align__(1024) unsigned char buf3[kLinStages >= 4 ? kStageBytes : 16];
   const int nt = p.n_tiles, tiles = p.m_tiles * nt;
   const int group = kLinGroupRows * nt, slots = linear_tile_slots(p.m_tiles, nt);
   const int bid = blockIdx.x;
@@ -304,7 +300,7 @@ __global__ __launch_bounds__(kLinThreads, 1) void linear_kernel(LinearParams p) 
   const int mb = t / nt, nb = t - mb * nt;
   const int M = p.m_count ? min(*p.m_count, p.M) : p.M;
   if (mb * kLinBM >= M) return;
-  linear_tile<DT>(p, mb, nb, M, buf0, buf1, buf2);
+  linear_tile<DT>(p, mb, nb, M, buf0, buf1, buf2, buf3);
 }
 
 hipError_t launch_linear(const LinearParams& p, int dtype, hipStream_t s) {
