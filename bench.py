@@ -339,6 +339,47 @@ def measure_block(ctx, reps, layers=12):
     return res
 
 
+def measure_ceilings(ctx):
+    """What this machine reaches on plain streaming and dense-matrix work, as
+    context for the fractions of the published peaks: a 1 GiB device copy
+    (read + write counted), a 1 GiB read (sum) and a 8192^3 fp16 product
+    through the vendor library."""
+    t = ctx.torch
+    a = t.ones(1 << 28, dtype=t.float32, device=ctx.dev)
+    b = t.empty_like(a)
+    rows = a.view(-1, 1 << 16)  # a row-wise sum reads everything with many workgroups
+    sink = t.empty(rows.shape[0], dtype=t.float32, device=ctx.dev)
+    nbytes = a.numel() * 4
+
+    def timed(fn, reps):
+        for _ in range(3):
+            fn()
+        return ctx.events_time(fn, reps)
+    copy_us = timed(lambda: b.copy_(a), 10)
+    read_us = timed(lambda: t.sum(rows, dim=1, out=sink), 10)
+    del a, b, rows
+    m = t.randn(8192, 8192, dtype=t.float16, device=ctx.dev)
+    mm_us = timed(lambda: t.matmul(m, m), 5)
+    del m
+    return {"copy_GBps": round(2 * nbytes / (copy_us * 1e-6) / 1e9, 1),
+            "read_GBps": round(nbytes / (read_us * 1e-6) / 1e9, 1),
+            "fp16_matmul_8192_TFLOPs": round(2 * 8192 ** 3 / (mm_us * 1e-6) / 1e12, 1)}
+
+
+def measure_floor_cpp():
+    """The C++ probe's dispatch floor (csrc/floor_bench.cpp, built next to the
+    library), run as a child process; None when it has not been built."""
+    import subprocess
+    exe = os.path.join(ROOT, "ragged_variable_length_amd", "floor_bench")
+    if not os.path.exists(exe):
+        return None
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    if r.returncode != 0:
+        log("floor_bench failed:", r.stderr.strip())
+        return None
+    return json.loads(r.stdout.strip().splitlines()[-1])
+
+
 def measure_floor(ctx, reps):
     rva = ctx.rva
     plan = rva.Plan(rva.EMPTY)
@@ -573,7 +614,10 @@ def main():
     reps = 200
     if not args.quick:
         floor = measure_floor(ctx, reps)
+        floor["cpp"] = measure_floor_cpp()
         line["launch_floor"] = floor
+        line["ceilings"] = measure_ceilings(ctx)
+        torch.cuda.empty_cache()
         per = []
         for wk in W.all_configs():
             log(f"measuring {wk.name} ...")

@@ -20,16 +20,36 @@ def hipcc_command(out=LIB):
         [os.path.join(PKG, s) for s in SOURCES] + ["-o", out]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source into librva.so next to this file; returns its path."""
-    tmp = LIB + ".tmp"
-    cmd = hipcc_command(tmp)
+FLOOR_BENCH = os.path.join(PKG, "floor_bench")
+
+
+def floor_bench_command(out=FLOOR_BENCH):
+    """The C++ dispatch-floor probe (csrc/floor_bench.cpp),
+    linked against librva.so in this directory."""
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    return [hipcc, "--offload-arch=gfx950", "-O2", "-std=c++17",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-I", os.path.join(ROOT, "include"), os.path.join(PKG, "csrc", "floor_bench.cpp"),
+            "-L", PKG, "-lrva", "-Wl,-rpath,$ORIGIN", "-o", out]
+
+
+def _run(cmd, out):
+    tmp = out + ".tmp"
+    cmd = cmd[:-1] + [tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + r.stdout + r.stderr)
+    os.replace(tmp, out)
+    return r
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source into librva.so next to this file (and the
+    dispatch-floor probe linked against it); returns the library's path."""
+    r = _run(hipcc_command(LIB), LIB)
     if verbose:
         print(r.stderr)
-    os.replace(tmp, LIB)
+    _run(floor_bench_command(), FLOOR_BENCH)
     return LIB
 
 
