@@ -6,15 +6,20 @@
 //
 // Work decomposition (CDNA4 / gfx950), 16-bit inputs:
 //  * one workgroup of 4 waves per (image, head); on large batches the fused
-//    form gives a workgroup two heads of one image in turn, so that its mask
-//    row is read and compacted once for both.  Post-pruning ViT sequences
-//    are short (at most 197 tokens at 224x224, 577 at 384x384), so the
-//    workgroup stages its sequence's K and V in LDS in one memory round trip,
-//    by direct-to-LDS loads; sequences longer than one chunk are staged in
-//    chunks.  V stays row-major and the V^T operand comes from the
-//    transposed LDS read;
-//  * each wave owns two query blocks of 16 rows at a time and walks the keys
-//    32 at a time;
+//    form gives a workgroup two heads of one image, so that its mask row is
+//    read and compacted once for both (the images dispatched last keep one
+//    head per workgroup, so the launch ends on short workgroups).
+//    Post-pruning ViT sequences are short (at most 197 tokens at 224x224,
+//    577 at 384x384): a sequence of up to rc rows (208 at N = 197, the most
+//    LDS that keeps 3 workgroups per CU) is staged whole, K and V of one or
+//    both heads in a single memory round trip by direct-to-LDS loads, with
+//    every query block's Q rows loaded alongside; longer sequences are
+//    staged in chunks.  V stays row-major and the V^T operand comes from
+//    the transposed LDS read;
+//  * a wave takes its query blocks of 16 rows one at a time when the
+//    sequence is staged whole (two at a time in the chunked form) and walks
+//    the keys 32 at a time, reading the next tile's K fragments while the
+//    current tile's softmax runs;
 //  * scores are formed transposed, S^T = K Q^T, with the 16x16x32 matrix-core
 //    product: each lane then holds one query and 4+4 keys, which is exactly
 //    the per-lane slice the second product O^T = V^T P^T takes as its B
@@ -167,31 +172,32 @@ __device__ __forceinline__ int kvswz(int row, int piece) { return row * 128 + ((
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 LdsS16x4;
 
+// K fragments of the 32-key tile at k0: lane (r16, g) holds
+// K[k0 + 16 kb + r16][32 ks + 8 g .. + 7] (A operand of S^T = K Q^T).
 template <int DT>
-__device__ __forceinline__ void tile16(const unsigned char* __restrict__ Ks,
-                                       const unsigned char* __restrict__ Vs, int k0, int kvalid,
-                                       const typename Half16<DT>::V8 (&qf)[2][2], f32x4 (&o)[2][5],
-                                       float (&m)[2], bool two, float c) {
-  typedef Half16<DT> Tr;
-  typedef typename Tr::T T;
-  typedef typename Tr::V8 V8;
-  typedef typename Tr::V4 V4;
+__device__ __forceinline__ void k_frag16(const unsigned char* __restrict__ Ks, int k0,
+                                         typename Half16<DT>::V8 (&kf)[2][2]) {
+  typedef typename Half16<DT>::V8 V8;
   const int lane = lane_id(), g = lane >> 4, r16 = lane & 15;
-  // A operand of S^T = K Q^T: lane (r16, g) holds K[k0 + 16 kb + r16][32 ks + 8 g .. + 7]
-  V8 kf[2][2];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
       kf[kb][ks] = *reinterpret_cast<const V8*>(Ks + kvswz(k0 + kb * 16 + r16, ks * 4 + g));
-  // A operand of O^T = V^T P^T: lane (r16, g) holds V[key][16 db + r16] for
-  // keys k0 + 4g + j and k0 + 16 + 4g + j (j < 4), the keys whose
-  // probabilities this lane's column of P^T carries.  The transposed LDS read
-  // hands lane i of a 16-lane group element i % 4 of the 8-byte pieces
-  // addressed by the group's lanes 4k + i / 4 (k < 4), so lane s addresses key
-  // row k0 + 4g + s / 4 at dims 16 db + 4 (s % 4) .. + 3.
+}
+
+// V fragments of the tile at k0 (A operand of O^T = V^T P^T): lane (r16, g)
+// holds V[key][16 db + r16] for keys k0 + 4g + j and k0 + 16 + 4g + j
+// (j < 4), the keys whose probabilities this lane's column of P^T carries.
+// The transposed LDS read hands lane i of a 16-lane group element i % 4 of
+// the 8-byte pieces addressed by the group's lanes 4k + i / 4 (k < 4), so
+// lane s addresses key row k0 + 4g + s / 4 at dims 16 db + 4 (s % 4) .. + 3.
+template <int DT>
+__device__ __forceinline__ void v_frag16(const unsigned char* __restrict__ Vs, int k0,
+                                         typename Half16<DT>::V8 (&vf)[4]) {
+  typedef typename Half16<DT>::V4 V4;
+  const int lane = lane_id(), g = lane >> 4, r16 = lane & 15;
   const int trow = k0 + 4 * g + (r16 >> 2), tcol = r16 & 3;
-  V8 vf[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) {
     const int piece = 2 * db + (tcol >> 1), half = (tcol & 1) << 3;
@@ -201,27 +207,157 @@ __device__ __forceinline__ void tile16(const unsigned char* __restrict__ Ks,
         (LdsS16x4*)(Vs + kvswz(trow + 16, piece) + half)));
     vf[db] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   }
+}
+
+// The per-lane parts of the fragment addresses of a tile.  Tiles start at
+// multiples of 32 rows, so a row's swizzle (row & 7) does not depend on the
+// tile, and fragment reads of the tile at k0 are (staging base + 128 k0)
+// plus these offsets plus constants.  Keeping them apart from the uniform
+// tile base lets every query block of a wave share one set of offsets.
+struct FragLanes16 {
+  uint32_t k[2];  // K: row r16, piece 4 ks + g
+  uint32_t v[4];  // V^T: row 4 g + r16 / 4, piece 2 db + (r16 & 3) / 2, half (r16 & 1)
+};
+
+__device__ __forceinline__ FragLanes16 frag_lanes16() {
+  const int lane = lane_id(), g = lane >> 4, r16 = lane & 15;
+  FragLanes16 L;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    if (i == 1 && !two) break;
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-    s0 = Tr::mfma(kf[0][0], qf[i][0], s0);
-    s1 = Tr::mfma(kf[1][0], qf[i][0], s1);
-    s0 = Tr::mfma(kf[0][1], qf[i][1], s0);
-    s1 = Tr::mfma(kf[1][1], qf[i][1], s1);
-    float pr[8];
-    softmax_step16(s0, s1, kvalid, c, m[i], o[i], pr);
-    V8 pf;
+  for (int ks = 0; ks < 2; ++ks) L.k[ks] = (uint32_t)kvswz(r16, ks * 4 + g);
+  const int trow = 4 * g + (r16 >> 2), tcol = r16 & 3;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) pf[j] = (T)pr[j];
+  for (int db = 0; db < 4; ++db)
+    L.v[db] = (uint32_t)(kvswz(trow, 2 * db + (tcol >> 1)) + ((tcol & 1) << 3));
+  return L;
+}
+
+// k_frag16 / v_frag16 through precomputed lane offsets; `tile` is the
+// tile's first row in the staging area (K or V) and goes through a
+// first-lane read so that it stays a uniform scalar added to fixed lane
+// offsets, rather than being folded into per-lane induction variables.
+template <int DT>
+__device__ __forceinline__ void k_frag16(const unsigned char* __restrict__ Ks, int tile,
+                                         const FragLanes16& L, typename Half16<DT>::V8 (&kf)[2][2]) {
+  typedef typename Half16<DT>::V8 V8;
+  const unsigned char* base = Ks + __builtin_amdgcn_readfirstlane(tile * kHeadDim * 2);
 #pragma unroll
-    for (int db = 0; db < 4; ++db) o[i][db] = Tr::mfma(vf[db], pf, o[i][db]);
-    // row sums of the rounded probabilities: every row of an all-ones A
-    // operand yields sum_k P[q][k], so each lane ends up holding its query's sum
-    V8 ones;
+  for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) ones[j] = (T)1.0f;
-    o[i][4] = Tr::mfma(ones, pf, o[i][4]);
+    for (int ks = 0; ks < 2; ++ks)
+      kf[kb][ks] = *reinterpret_cast<const V8*>(base + L.k[ks] + kb * 16 * kHeadDim * 2);
+}
+
+// `upper` = the tile's keys 16..31 are staged; otherwise their V operand is
+// zero (their probabilities are zero too) and nothing past the staged rows
+// is read.
+template <int DT>
+__device__ __forceinline__ void v_frag16(const unsigned char* __restrict__ Vs, int tile,
+                                         const FragLanes16& L, bool upper,
+                                         typename Half16<DT>::V8 (&vf)[4]) {
+  typedef typename Half16<DT>::V4 V4;
+  const unsigned char* base = Vs + __builtin_amdgcn_readfirstlane(tile * kHeadDim * 2);
+  V4 hi[4];
+  if (upper) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+      hi[db] = __builtin_bit_cast(V4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (LdsS16x4*)(base + L.v[db] + 16 * kHeadDim * 2)));
+  } else {
+#pragma unroll
+    for (int db = 0; db < 4; ++db) hi[db] = V4{};
+  }
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    const V4 lo = __builtin_bit_cast(V4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (LdsS16x4*)(base + L.v[db])));
+    vf[db] = __builtin_shufflevector(lo, hi[db], 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+}
+
+// LDS fragments of one 32-key tile, shared by every query block that a wave
+// runs against that tile.
+template <int DT>
+struct KVFrag16 {
+  typename Half16<DT>::V8 kf[2][2];
+  typename Half16<DT>::V8 vf[4];
+};
+
+template <int DT>
+__device__ __forceinline__ KVFrag16<DT> kv_frag16(const unsigned char* __restrict__ Ks,
+                                                  const unsigned char* __restrict__ Vs, int k0) {
+  KVFrag16<DT> f;
+  k_frag16<DT>(Ks, k0, f.kf);
+  v_frag16<DT>(Vs, k0, f.vf);
+  return f;
+}
+
+// Scores of one 16-query block against one 32-key tile, transposed:
+// s0 = keys 4g..4g+3, s1 = keys 16+4g..16+4g+3 of this lane's query.  qf is
+// the B operand: lane (r16, g) holds Q[q][32 ks + 8 g .. + 7].
+template <int DT>
+__device__ __forceinline__ void scores16(const typename Half16<DT>::V8 (&kf)[2][2],
+                                         const typename Half16<DT>::V8 (&qf)[2], f32x4& s0,
+                                         f32x4& s1) {
+  typedef Half16<DT> Tr;
+  s0 = f32x4{0.f, 0.f, 0.f, 0.f};
+  s1 = f32x4{0.f, 0.f, 0.f, 0.f};
+  s0 = Tr::mfma(kf[0][0], qf[0], s0);
+  s1 = Tr::mfma(kf[1][0], qf[0], s1);
+  s0 = Tr::mfma(kf[0][1], qf[1], s0);
+  s1 = Tr::mfma(kf[1][1], qf[1], s1);
+}
+
+// Online softmax of the tile's scores and the accumulation of O^T (o[0..3])
+// and of the probability row sums (o[4]).
+template <int DT>
+__device__ __forceinline__ void prob_step16(const typename Half16<DT>::V8 (&vf)[4], f32x4& s0,
+                                            f32x4& s1, f32x4 (&o)[5], float& m, int kvalid,
+                                            float c) {
+  typedef Half16<DT> Tr;
+  typedef typename Tr::T T;
+  typedef typename Tr::V8 V8;
+  float pr[8];
+  softmax_step16(s0, s1, kvalid, c, m, o, pr);
+  V8 pf;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) pf[j] = (T)pr[j];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) o[db] = Tr::mfma(vf[db], pf, o[db]);
+  // row sums of the rounded probabilities: every row of an all-ones A
+  // operand yields sum_k P[q][k], so each lane ends up holding its query's sum
+  V8 ones;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) ones[j] = (T)1.0f;
+  o[4] = Tr::mfma(ones, pf, o[4]);
+}
+
+// One 16-query block against one 32-key tile.
+template <int DT>
+__device__ __forceinline__ void block_step16(const KVFrag16<DT>& f,
+                                             const typename Half16<DT>::V8 (&qf)[2], f32x4 (&o)[5],
+                                             float& m, int kvalid, float c) {
+  f32x4 s0, s1;
+  scores16<DT>(f.kf, qf, s0, s1);
+  prob_step16<DT>(f.vf, s0, s1, o, m, kvalid, c);
+}
+
+// Normalise one finished query block and store its rows: O^T block db,
+// lane (r16, g) holds O[q][16 db + 4 g .. + 3]; o[4] holds the query's
+// probability sum in every element.  Rows at kOOB are dropped.
+template <int DT>
+__device__ __forceinline__ void store_block16(const f32x4 (&o)[5], Rsrc ro, uint32_t qoff) {
+  typedef Half16<DT> Tr;
+  typedef typename Tr::T T;
+  typedef typename Tr::V4 V4;
+  const int g = lane_id() >> 4;
+  const float inv = 1.f / o[4][0];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    V4 out;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) out[j] = (T)(o[db][j] * inv);
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, out), ro,
+                                          (int)(qoff + db * 32 + 8 * g), 0, 0);
   }
 }
 
@@ -235,18 +371,19 @@ __device__ __forceinline__ void tile16(const unsigned char* __restrict__ Ks,
 // i.e. row L / 8, slot L % 8; the lane fetches the 16-byte piece that the
 // row swizzle puts in that slot.  Every row offset is read (through roff)
 // before the first load is issued, so no load waits behind another's LDS
-// write.  Keys in [rows, round_up(rows, 32)) are out of range and land as
+// write.  Keys in [rows, round_up(rows, pad)) are out of range and land as
 // zeros, so masked probabilities (exact zeros) never meet stale LDS
 // contents.  The caller's barrier (with its memory fence) makes the chunk
-// visible.  `roff(r)` is the byte offset of sequence row r.
-template <int DT, typename RowOff>
+// visible.  `roff(r)` is the byte offset of sequence row r; MAXROWS bounds
+// round_up(rows, pad).
+template <int DT, int MAXROWS, typename RowOff>
 __device__ __forceinline__ void stage16(Rsrc rk, Rsrc rv, unsigned char* Ks, unsigned char* Vs,
-                                        int c0, int rows, RowOff roff) {
+                                        int c0, int rows, int pad, RowOff roff) {
   constexpr int kWaves = kAttnThreads16 / 64;
-  constexpr int NI = kKcMax16 / 8 / kWaves;  // 8-row loads per wave, at most
-  static_assert(kKcMax16 % (8 * kWaves) == 0 && kKcMax16 % kKeyTile == 0, "whole loads");
+  constexpr int NI = MAXROWS / 8 / kWaves;  // 8-row loads per wave, at most
+  static_assert(MAXROWS % (8 * kWaves) == 0, "whole loads");
   const int lane = lane_id(), w = wave_id();
-  const int rpad = round_up(rows, kKeyTile);
+  const int rpad = round_up(rows, pad);
   const int rl = lane >> 3;                 // row within the load (row & 7 == rl)
   const uint32_t piece16 = (uint32_t)(((lane & 7) ^ rl) << 4);
   uint32_t off[NI];
@@ -315,7 +452,7 @@ __device__ __forceinline__ void attend_seq16(const AttnParams& p, int n, unsigne
       const int rows = min(kc, n - c0);
       if (!(pass > 0 && cc == 0)) {
         if (pass > 0 || cc > 0) __syncthreads();
-        stage16<DT>(rk, rv, Ks, Vs, c0, rows, roff);
+        stage16<DT, kKcMax16>(rk, rv, Ks, Vs, c0, rows, kKeyTile, roff);
         __syncthreads();
       }
       if (pass == npass - 1 && cc == nchunk - 1) last_use();
@@ -331,25 +468,110 @@ __device__ __forceinline__ void attend_seq16(const AttnParams& p, int n, unsigne
         const int ntile = (rows + kKeyTile - 1) / kKeyTile;
         for (int t = 0; t < ntile; ++t) {
           const int k0 = t * kKeyTile;
-          tile16<DT>(Ks, Vs, k0, min(kKeyTile, rows - k0), qf, o, m, act[1], c);
+          const int kvalid = min(kKeyTile, rows - k0);
+          const KVFrag16<DT> f = kv_frag16<DT>(Ks, Vs, k0);
+          block_step16<DT>(f, qf[0], o[0], m[0], kvalid, c);
+          if (act[1]) block_step16<DT>(f, qf[1], o[1], m[1], kvalid, c);
         }
       }
     }
-    // O^T block db, lane (r16, g) holds O[q][16 db + 4 g .. + 3]; o[i][4] holds
-    // the query's probability sum in every element.  Rows q >= n go to kOOB.
+    // rows q >= n went to kOOB
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      if (!act[i]) continue;
-      const float inv = 1.f / o[i][4][0];
+    for (int i = 0; i < 2; ++i)
+      if (act[i]) store_block16<DT>(o[i], ro, qoff[i]);
+  }
+}
+
+// Whole sequences resident in LDS (n <= rc): the K and V rows of `nh`
+// heads of one sequence are staged at once, each head as round_up(n, 16)
+// K rows followed by as many V rows (nh * round_up(n, 16) <= rc), each
+// wave loads the Q rows of its (head, query block) units before the
+// staging barrier, and then runs its units one at a time, storing each as
+// soon as it is done.  One memory round trip for all nh heads, however
+// many query blocks the sequence has.  Head j of the group lies j * 128
+// bytes after head 0 in every token row, so one set of descriptors (over
+// head 0's slice, sized to cover the group) and roff serve all of them.
+// A wave has at most 4 units (rc <= 256); three Q fragments are held at
+// once and the fourth unit's rows are loaded into the first unit's
+// registers as soon as that unit is done.
+constexpr int kUnitsPerWave = kResidentMax16 / kQBlock / (kAttnThreads16 / 64);
+constexpr int kQSlots = 3;
+
+template <int DT, typename RowOff, typename Hook>
+__device__ __forceinline__ void attend_resident16(int n, int nh, float c, unsigned char* kvbase,
+                                                  Rsrc rq, Rsrc rk, Rsrc rv, Rsrc ro, RowOff roff,
+                                                  Hook last_use) {
+  typedef Half16<DT> Tr;
+  typedef typename Tr::V8 V8;
+  constexpr int kWaves = kAttnThreads16 / 64;
+  constexpr uint32_t kHeadBytes = kHeadDim * 2;
+  static_assert(kUnitsPerWave == kQSlots + 1, "one late Q load per wave");
+  // n through an opaque (volatile) move: the unit arithmetic below then
+  // cannot be hoisted out of a caller's loop over head groups, where it
+  // would stay live across the loop and spill
+  asm volatile("" : "+s"(n));
+  const int lane = lane_id(), w = wave_id(), g = lane >> 4, r16 = lane & 15;
+  const int rows = round_up(n, kQBlock);  // staged rows per head, K and V each
+  const int nqb = rows / kQBlock;
+  const int nunits = nh * nqb;
+  // every kept-row offset is read before the staging barrier
+  uint32_t qoff[kUnitsPerWave];
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        V4 out;
+  for (int i = 0; i < kUnitsPerWave; ++i) {
+    const int u = w + i * kWaves;
+    const int hu = u / nqb;
+    const int q = (u - hu * nqb) * kQBlock + r16;
+    qoff[i] = (u < nunits && q < n) ? roff(q) + (uint32_t)hu * kHeadBytes : kOOB;
+  }
+  auto load_q = [&](uint32_t off, V8 (&qs)[2]) {
+    // B operand of S^T = K Q^T: lane (r16, g) holds Q[q][32 ks + 8 g .. + 7]
+    qs[0] = __builtin_bit_cast(V8, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)(off + 16 * g), 0, 0));
+    qs[1] = __builtin_bit_cast(V8, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)(off + 64 + 16 * g), 0, 0));
+  };
+  V8 qf[kQSlots][2];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) out[j] = (T)(o[i][db][j] * inv);
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, out), ro,
-                                              (int)(qoff[i] + db * 32 + 8 * g), 0, 0);
-      }
+  for (int i = 0; i < kQSlots; ++i) load_q(qoff[i], qf[i]);
+  for (int h = 0; h < nh; ++h) {
+    unsigned char* Ks = kvbase + h * rows * 2 * kHeadBytes;
+    const uint32_t hoff = (uint32_t)h * kHeadBytes;
+    stage16<DT, kResidentMax16>(rk, rv, Ks, Ks + rows * kHeadBytes, 0, n, kQBlock,
+                                [=](int r) -> uint32_t { return roff(r) + hoff; });
+  }
+  __syncthreads();
+  last_use();
+  const int ntile = (n + kKeyTile - 1) / kKeyTile;
+  const FragLanes16 lanes = frag_lanes16();
+#pragma unroll
+  for (int i = 0; i < kUnitsPerWave; ++i) {
+    const int u = w + i * kWaves;
+    if (u >= nunits) break;
+    const int slot = i % kQSlots;
+    if (i == 1 && w + kQSlots * kWaves < nunits) load_q(qoff[kQSlots], qf[0]);
+    const int hu = u / nqb;
+    const unsigned char* Ks = kvbase + hu * rows * 2 * kHeadBytes;
+    const unsigned char* Vs = Ks + rows * kHeadBytes;
+    f32x4 o[5];
+#pragma unroll
+    for (int db = 0; db < 5; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m = -INFINITY;
+    // Software-pipelined over the tiles: the next tile's K fragments are
+    // read right after this tile's score products issue, so their LDS
+    // latency hides behind the softmax instead of stalling the next
+    // products.  Every read stays inside the head's staged rows: a last
+    // tile with 16 staged rows reads its K rows 16..31 from the head's
+    // first V rows (their scores are masked) and skips their V rows.
+    V8 kf[2][2];
+    k_frag16<DT>(Ks, 0, lanes, kf);
+    for (int t = 0; t < ntile; ++t) {
+      const int k0 = t * kKeyTile;
+      V8 vf[4];
+      v_frag16<DT>(Vs, k0, lanes, k0 + kQBlock < rows, vf);
+      f32x4 s0, s1;
+      scores16<DT>(kf, qf[slot], s0, s1);
+      if (t + 1 < ntile) k_frag16<DT>(Ks, k0 + kKeyTile, lanes, kf);
+      prob_step16<DT>(vf, s0, s1, o, m, min(kKeyTile, n - k0), c);
     }
+    store_block16<DT>(o, ro, qoff[i]);
   }
 }
 
@@ -544,22 +766,56 @@ __device__ __forceinline__ void attend_body(const AttnParams& p, unsigned char* 
     }
   }
   // fused 16-bit: a workgroup may take several heads of one image in turn,
-  // so that the mask row is read and compacted once for all of them
-  const int HG = (FUSED && DT != 0) ? p.heads_per_wg : 1;
-  const int ngrp = (p.H + HG - 1) / HG;
-  const int b = bid / ngrp, hg = bid - b * ngrp;
+  // so that the mask row is read and compacted once for all of them; the
+  // last tail_b images of the batch (dispatched last) take one head per
+  // workgroup, so the launch ends on short workgroups
+  int HG = (FUSED && DT != 0) ? p.heads_per_wg : 1;
+  int b, hg;
+  {
+    const int ngrp = (p.H + HG - 1) / HG;
+    const int lead = (p.B - p.tail_b) * ngrp;
+    if (bid < lead) {
+      b = bid / ngrp;
+      hg = bid - b * ngrp;
+    } else {
+      const int r = bid - lead, bt = r / p.H;
+      b = p.B - p.tail_b + bt;
+      hg = r - bt * p.H;
+      HG = 1;
+    }
+  }
   const int H = p.H, N = p.N;
   constexpr int ES = DT == 0 ? 4 : 2;
   const uint32_t rs = (uint32_t)(H * kHeadDim);  // elements between consecutive token rows
   if constexpr (FUSED) {
-    int32_t* idx = reinterpret_cast<int32_t*>(smem);
-    const size_t off = (size_t)round_up(N * 4, 16);
-    uint64_t* ballots = reinterpret_cast<uint64_t*>(smem + off);
-    int32_t* cnt = reinterpret_cast<int32_t*>(smem + off + 16 * 8);
-    const int n = compact_row<NT>(p.mask + (size_t)b * N, N, idx, nullptr, ballots, cnt);
+    uint16_t* idx = reinterpret_cast<uint16_t*>(smem);
+    uint64_t* ballots = reinterpret_cast<uint64_t*>(smem + attn_ballots_off(N));
+    int32_t* cnt = reinterpret_cast<int32_t*>(smem + attn_cnt_off(N));
+    const int n = compact_row<NT, uint16_t>(p.mask + (size_t)b * N, N, idx, nullptr, ballots, cnt);
     unsigned char* kvbase = smem + attn_compact_bytes(N);
-    const int h1 = min(H, hg * HG + HG);
-    for (int h = hg * HG; h < h1; ++h) {
+    const int h0 = hg * HG, h1 = min(H, h0 + HG);
+    const uint32_t bytes = (uint32_t)N * rs * ES;
+    if constexpr (DT != 0) {
+      if (n > 0 && n <= p.rc) {
+        // whole sequence resident: as many of the group's heads at once as
+        // their K/V rows fit in the staging area
+        const int fit = p.rc / round_up(n, kQBlock);
+        auto roff = [=](int r) -> uint32_t { return (uint32_t)idx[min(r, n - 1)] * (rs * ES); };
+        for (int h = h0; h < h1;) {
+          const int nh = min(fit, h1 - h);
+          if (h > h0) __syncthreads();  // the previous heads' staged rows are consumed
+          const AttnParams pl = rebase(p, ((size_t)b * N * H + h) * kHeadDim, ES);
+          for (int j = 0; j < nh; ++j)
+            zero_pruned<NT, ES>(static_cast<char*>(pl.o) + j * kHeadDim * ES, ballots, N, H);
+          attend_resident16<DT>(n, nh, p.scale_log2e, kvbase, make_rsrc(pl.q, bytes),
+                                make_rsrc(pl.k, bytes), make_rsrc(pl.v, bytes),
+                                make_rsrc(pl.o, bytes), roff, [] {});
+          h += nh;
+        }
+        return;
+      }
+    }
+    for (int h = h0; h < h1; ++h) {
       if (h > hg * HG) __syncthreads();  // the previous head's staged rows are consumed
       const AttnParams pl = rebase(p, ((size_t)b * N * H + h) * kHeadDim, ES);
       zero_pruned<NT, ES>(static_cast<char*>(pl.o), ballots, N, H);
@@ -568,7 +824,6 @@ __device__ __forceinline__ void attend_body(const AttnParams& p, unsigned char* 
       if constexpr (DT == 0) {
         attend_seq32(pl, n, kvbase, elem);
       } else {
-        const uint32_t bytes = (uint32_t)N * rs * ES;
         auto roff = [=](int r) -> uint32_t { return (uint32_t)idx[min(r, n - 1)] * (rs * ES); };
         attend_seq16<DT>(pl, n, kvbase, make_rsrc(pl.q, bytes), make_rsrc(pl.k, bytes),
                          make_rsrc(pl.v, bytes), make_rsrc(pl.o, bytes), roff, [] {});
@@ -586,8 +841,13 @@ __device__ __forceinline__ void attend_body(const AttnParams& p, unsigned char* 
     } else {
       const uint32_t bytes = (uint32_t)n * rs * ES;
       auto roff = [=](int r) -> uint32_t { return (uint32_t)r * (rs * ES); };
-      attend_seq16<DT>(pl, n, smem, make_rsrc(pl.q, bytes), make_rsrc(pl.k, bytes),
-                       make_rsrc(pl.v, bytes), make_rsrc(pl.o, bytes), roff, [] {});
+      if (n <= p.rc)
+        attend_resident16<DT>(n, 1, p.scale_log2e, smem, make_rsrc(pl.q, bytes),
+                              make_rsrc(pl.k, bytes), make_rsrc(pl.v, bytes),
+                              make_rsrc(pl.o, bytes), roff, [] {});
+      else
+        attend_seq16<DT>(pl, n, smem, make_rsrc(pl.q, bytes), make_rsrc(pl.k, bytes),
+                         make_rsrc(pl.v, bytes), make_rsrc(pl.o, bytes), roff, [] {});
     }
   }
 }
@@ -655,10 +915,9 @@ __global__ __launch_bounds__(kAttnThreads16, 3) void attend16_persistent_kernel(
           a0 + (uint32_t)(dw0 + lane) * 4, 0, 0, 0);
     }
   };
-  int32_t* idx = reinterpret_cast<int32_t*>(smem);
-  const size_t off = (size_t)round_up(N * 4, 16);
-  uint64_t* ballots = reinterpret_cast<uint64_t*>(smem + off);
-  int32_t* cnt = reinterpret_cast<int32_t*>(smem + off + 16 * 8);
+  uint16_t* idx = reinterpret_cast<uint16_t*>(smem);
+  uint64_t* ballots = reinterpret_cast<uint64_t*>(smem + attn_ballots_off(N));
+  int32_t* cnt = reinterpret_cast<int32_t*>(smem + attn_cnt_off(N));
   unsigned char* kvbase = smem + attn_compact_bytes(N);
   // compaction of `item` from the prefetched row (its last bytes past the
   // final whole dword of the mask tensor straight from memory)
@@ -672,7 +931,7 @@ __global__ __launch_bounds__(kAttnThreads16, 3) void attend16_persistent_kernel(
       mb[i] = 0;
       if (j < N) mb[i] = start + (uint32_t)j < mask_tail ? row[j] : p.mask[start + j];
     }
-    return compact_bytes<NT>(mb, N, idx, nullptr, ballots, cnt);
+    return compact_bytes<NT, uint16_t>(mb, N, idx, nullptr, ballots, cnt);
   };
 
   if (tid == 0) s_item = atomicAdd(p.work, 1);
@@ -703,8 +962,13 @@ __global__ __launch_bounds__(kAttnThreads16, 3) void attend16_persistent_kernel(
     if (n > 0) {
       const uint32_t bytes = (uint32_t)N * rs * ES;
       auto roff = [=](int r) -> uint32_t { return (uint32_t)idx[min(r, n - 1)] * (rs * ES); };
-      attend_seq16<DT>(pl, n, kvbase, make_rsrc(pl.q, bytes), make_rsrc(pl.k, bytes),
-                       make_rsrc(pl.v, bytes), make_rsrc(pl.o, bytes), roff, next_ready);
+      if (n <= p.rc)
+        attend_resident16<DT>(n, 1, p.scale_log2e, kvbase, make_rsrc(pl.q, bytes),
+                              make_rsrc(pl.k, bytes), make_rsrc(pl.v, bytes),
+                              make_rsrc(pl.o, bytes), roff, next_ready);
+      else
+        attend_seq16<DT>(pl, n, kvbase, make_rsrc(pl.q, bytes), make_rsrc(pl.k, bytes),
+                         make_rsrc(pl.v, bytes), make_rsrc(pl.o, bytes), roff, next_ready);
     } else {
       __syncthreads();  // every wave's zero fill read the ballots; fetch and prefetch landed
       next_ready();
@@ -727,14 +991,34 @@ __global__ __launch_bounds__(kAttnThreads16, 3) void attend16_persistent_kernel(
   }
 }
 
-int attend_persistent_per_cu(int N, int kc) {
-  const size_t lds = attn_lds_bytes(1, true, N, kc) + kPersistentStaticLds;
-  const int by_lds = (int)((160 * 1024) / lds);
-  return by_lds < 3 ? by_lds : 3;  // 3 waves per SIMD by registers
+// Rows of the 16-bit staging area a launch gives whole sequences: kc when
+// the length hint is below the chunk cap; otherwise as many 16-row blocks
+// as the LDS left to each of 3 workgroups per CU holds (after the
+// compaction area and static LDS), at most kResidentMax16.  At N = 197
+// that is 208 rows: 53248 bytes of K/V and 448 of compaction area.
+static int resident_rows(int dtype, bool fused, int N, int kc, int static_bytes) {
+  if (dtype == 0) return 0;
+  if (kc < kKcMax16) return kc;
+  const long long per_wg = (long long)kLdsPerWg16 - static_bytes -
+                           (fused ? (long long)attn_compact_bytes(N) : 0);
+  int rows = (int)(per_wg / (kHeadDim * 2 * 2)) / kQBlock * kQBlock;
+  if (rows > kResidentMax16) rows = kResidentMax16;
+  return rows > kc ? rows : kc;
 }
 
-hipError_t launch_attend_persistent(const AttnParams& p, int dtype, int grid, hipStream_t s) {
-  const size_t lds = attn_lds_bytes(dtype, true, p.N, p.kc);
+static int kv_rows(int dtype, int kc, int rc) { return dtype == 0 ? kc : (rc > kc ? rc : kc); }
+
+int attend_persistent_per_cu(int N, int kc) {
+  const int rc = resident_rows(1, true, N, kc, kPersistentStaticLds);
+  const size_t lds = attn_lds_bytes(1, true, N, kv_rows(1, kc, rc)) + kPersistentStaticLds;
+  const int by_lds = (int)(kLdsPerCu / lds);
+  return by_lds < kAttnWgPerCu16 ? by_lds : kAttnWgPerCu16;  // 3 waves per SIMD by registers
+}
+
+hipError_t launch_attend_persistent(const AttnParams& p0, int dtype, int grid, hipStream_t s) {
+  AttnParams p = p0;
+  p.rc = resident_rows(dtype, true, p.N, p.kc, kPersistentStaticLds);
+  const size_t lds = attn_lds_bytes(dtype, true, p.N, kv_rows(dtype, p.kc, p.rc));
   if (dtype == 1)
     hipLaunchKernelGGL((attend16_persistent_kernel<1>), dim3(grid), dim3(kAttnThreads16), lds, s, p);
   else
@@ -745,7 +1029,7 @@ hipError_t launch_attend_persistent(const AttnParams& p, int dtype, int grid, hi
 // Dynamic LDS limit: the 160 KB of a CU minus the kernel's static LDS.
 static hipError_t set_lds_limit(const void* fn, int static_bytes = 0) {
   return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
-                             160 * 1024 - static_bytes);
+                             kLdsPerCu - static_bytes);
 }
 
 hipError_t attend_init() {
@@ -767,10 +1051,14 @@ hipError_t attend_init() {
   return hipSuccess;
 }
 
-hipError_t launch_attend(const AttnParams& p, int dtype, bool fused, hipStream_t s) {
-  const size_t lds = attn_lds_bytes(dtype, fused, p.N, p.kc);
+hipError_t launch_attend(const AttnParams& p0, int dtype, bool fused, hipStream_t s) {
+  AttnParams p = p0;
+  p.rc = resident_rows(dtype, fused, p.N, p.kc, 0);
+  const size_t lds = attn_lds_bytes(dtype, fused, p.N, kv_rows(dtype, p.kc, p.rc));
   const int hg = (fused && dtype != 0) ? p.heads_per_wg : 1;
-  const int grid = p.B * ((p.H + hg - 1) / hg) + ((fused && (p.cu_out || p.max_out)) ? 1 : 0);
+  const int tail = (fused && dtype != 0) ? p.tail_b : 0;
+  const int grid = (p.B - tail) * ((p.H + hg - 1) / hg) + tail * p.H +
+                   ((fused && (p.cu_out || p.max_out)) ? 1 : 0);
   const dim3 blk(attn_threads(dtype));
   if (dtype == 0) {
     if (fused) hipLaunchKernelGGL((attend32_kernel<true>), dim3(grid), blk, lds, s, p);

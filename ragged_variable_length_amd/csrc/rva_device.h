@@ -210,10 +210,11 @@ __device__ __forceinline__ void mask_row_bytes(const uint8_t* __restrict__ mrow,
 // takes 64-token chunks; a ballot gives every kept lane its rank inside the
 // chunk, a prefix over the (at most 16) chunk counts gives the chunk's base.
 // Optionally stores rank[j] (-1 for a pruned token) and the per-chunk
-// ballots.  `cnt` holds 16 ints.  Contains two barriers; every thread must
-// call it.
-template <int NT>
-__device__ int compact_bytes(const uint8_t (&mb)[compact_per<NT>()], int N, int32_t* idx,
+// ballots.  `cnt` holds one int per 64-token chunk.  Idx is int32_t or
+// uint16_t (positions are below 1024).  Contains two barriers; every
+// thread must call it.
+template <int NT, typename Idx = int32_t>
+__device__ int compact_bytes(const uint8_t (&mb)[compact_per<NT>()], int N, Idx* idx,
                              int32_t* rank, uint64_t* ballots, int32_t* cnt) {
   constexpr int W = NT / 64;
   constexpr int PER = compact_per<NT>();
@@ -242,7 +243,7 @@ __device__ int compact_bytes(const uint8_t (&mb)[compact_per<NT>()], int N, int3
       for (int cc = 0; cc < c; ++cc) base += cnt[cc];
       const int j = c * 64 + lane;
       const int r = base + __popcll(bal[i] & lanemask_lt());
-      if (keep[i]) idx[r] = j;
+      if (keep[i]) idx[r] = (Idx)j;
       if (rank && j < N) rank[j] = keep[i] ? r : -1;
     }
   }
@@ -250,12 +251,12 @@ __device__ int compact_bytes(const uint8_t (&mb)[compact_per<NT>()], int N, int3
   return n;
 }
 
-template <int NT>
-__device__ int compact_row(const uint8_t* __restrict__ mrow, int N, int32_t* idx, int32_t* rank,
+template <int NT, typename Idx = int32_t>
+__device__ int compact_row(const uint8_t* __restrict__ mrow, int N, Idx* idx, int32_t* rank,
                            uint64_t* ballots, int32_t* cnt) {
   uint8_t mb[compact_per<NT>()];
   mask_row_bytes<NT>(mrow, N, mb);
-  return compact_bytes<NT>(mb, N, idx, rank, ballots, cnt);
+  return compact_bytes<NT, Idx>(mb, N, idx, rank, ballots, cnt);
 }
 
 }  // namespace rva

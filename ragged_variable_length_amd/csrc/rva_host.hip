@@ -390,12 +390,19 @@ int enqueue_attend(const rva::AttnParams& p0, int dtype, bool fused, hipStream_t
   RVA_TRY(ensure_init());
   rva::AttnParams p = p0;
   p.heads_per_wg = 1;
+  p.tail_b = 0;
   if (fused && dtype != RVA_F32 && p.H > 1) {
     // pair the heads of an image only when the pairs still fill every
-    // resident slot (3 per CU) at least twice over
+    // resident slot (3 per CU) at least twice over; the images dispatched
+    // last (about two slot-fills of single heads) stay unpaired
     int cus = 0;
     RVA_TRY(device_cus(&cus));
-    if ((long long)p.B * ((p.H + 1) / 2) >= 2LL * 3 * cus) p.heads_per_wg = 2;
+    const long long slots = 3LL * cus;
+    if ((long long)p.B * ((p.H + 1) / 2) >= 2 * slots) {
+      p.heads_per_wg = 2;
+      const long long t = (2 * slots + p.H - 1) / p.H;
+      p.tail_b = (int)(t < p.B ? t : p.B);
+    }
   }
   hipError_t e = rva::launch_attend(p, dtype, fused, s);
   if (e != hipSuccess) return hip_fail(e, fused ? "fused launch" : "attention launch");

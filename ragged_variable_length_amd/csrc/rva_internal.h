@@ -21,6 +21,16 @@ constexpr int kScanThreads = 1024;
 // (16-byte pieces XOR-swizzled by row); fp32: K and V rows [kc][68] floats.
 constexpr int kKcMax16 = 192;
 constexpr int kKcMax32 = 128;
+// 16-bit sequences of up to rc rows are staged whole (K and V of one head
+// in one round trip); rc is capped by the registers' query blocks (4 per
+// wave, 4 waves) and by the LDS that keeps 3 workgroups per CU.
+constexpr int kResidentMax16 = 256;
+constexpr int kLdsPerCu = 160 * 1024;
+constexpr int kAttnWgPerCu16 = 3;
+// LDS is given to workgroups in 1280-byte granules (a CU's 160 KB in 128
+// of them): 3 workgroups fit a CU at up to 42 granules (53760 bytes) each.
+constexpr int kLdsGranule = 1280;
+constexpr int kLdsPerWg16 = kLdsPerCu / kAttnWgPerCu16 / kLdsGranule * kLdsGranule;
 constexpr int kPitch32 = 68;   // floats per staged K/V row for fp32
 
 struct AttnParams {
@@ -37,6 +47,8 @@ struct AttnParams {
   float scale_log2e;      // softmax scale * log2(e)
   int32_t* work;          // persistent form: [next item, workgroups done], zero between launches
   int heads_per_wg;       // fused 16-bit form: heads of one image a workgroup takes in turn (>= 1)
+  int rc;                 // 16-bit: longest sequence staged whole (rows, multiple of 16, >= kc); set at launch
+  int tail_b;             // fused 16-bit form: last images taken one head per workgroup (0..B)
 };
 
 struct CopyParams {
@@ -77,16 +89,20 @@ __host__ __device__ inline int round_up(int x, int m) { return (x + m - 1) / m *
 
 inline int attn_kc_max(int dtype) { return dtype == 0 ? kKcMax32 : kKcMax16; }
 
-// Bytes of the compaction area at the start of the fused kernel's LDS:
-// kept list int32[N], 16 per-chunk ballots (u64), 16 chunk counts (int32).
+// Compaction area at the start of the fused kernel's LDS: the kept list
+// uint16[N], then one ballot (u64) and one count (int32) per 64-token chunk.
+__host__ __device__ inline int attn_chunks(int N) { return (N + 63) >> 6; }
+__host__ __device__ inline size_t attn_ballots_off(int N) { return (size_t)round_up(N * 2, 16); }
+__host__ __device__ inline size_t attn_cnt_off(int N) { return attn_ballots_off(N) + (size_t)attn_chunks(N) * 8; }
 __host__ __device__ inline size_t attn_compact_bytes(int N) {
-  return (size_t)round_up(N * 4, 16) + 16 * 8 + 16 * 4;
+  return (size_t)round_up((int)attn_cnt_off(N) + attn_chunks(N) * 4, 16);
 }
 
 inline int attn_threads(int dtype) { return dtype == 0 ? kAttnThreads32 : kAttnThreads16; }
 
-inline size_t attn_lds_bytes(int dtype, bool fused, int N, int kc) {
-  size_t kv = dtype == 0 ? (size_t)kc * kPitch32 * 4 * 2 : (size_t)kc * kHeadDim * 2 * 2;
+// kv_rows: staged key rows (kc for fp32; max(kc, rc) for 16-bit).
+inline size_t attn_lds_bytes(int dtype, bool fused, int N, int kv_rows) {
+  size_t kv = dtype == 0 ? (size_t)kv_rows * kPitch32 * 4 * 2 : (size_t)kv_rows * kHeadDim * 2 * 2;
   size_t head = fused ? attn_compact_bytes(N) : 0;
   size_t scan = (size_t)(4 * attn_threads(dtype) + 64) * 4;  // fused scan workgroup reuses LDS
   size_t total = head + kv;

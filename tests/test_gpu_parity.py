@@ -181,6 +181,39 @@ def test_chunked_staging(device, name, hint):
     assert max_err(f64(o2[:T]), ref_pk) <= TOL[w.dtype]
 
 
+RESIDENT_EDGES = [1, 15, 16, 17, 31, 32, 33, 47, 48, 63, 64, 65, 95, 96, 97, 103, 104, 105, 112,
+                  127, 128, 129, 160, 176, 191, 192, 193, 200, 207, 208, 209, 223, 224, 0]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_resident_boundaries(device, dtype):
+    """Kept counts on every 16- and 32-row boundary up to the padded length,
+    in a batch large enough that the fused form pairs heads (5 heads, so the
+    last group has one): sequences staged whole one or two heads at a time,
+    with a fourth query block per wave, and past the whole-sequence capacity
+    in chunks.  Fused and packed forms against the oracle, every row."""
+    rva = _rva()
+    B, N, H = 512, 224, 5
+    counts = [RESIDENT_EDGES[b % len(RESIDENT_EDGES)] for b in range(B)]
+    w = W.random_workload(31 if dtype == "f16" else 32, B=B, N=N, H=H, dtype=dtype,
+                          counts=counts, name=f"resident_{dtype}")
+    _say(f"[resident] {dtype} B={B} N={N} H={H}")
+    q, k, v, mask = upload(w, device)
+    o = torch.full_like(q, float("nan"))
+    rva.fused(q, k, v, mask, out=o)
+    pk = rva.pack(q, k, v, mask)
+    o2 = rva.ragged_attend(pk["q"], pk["k"], pk["v"], pk["cu_seqlens"], N)
+    torch.cuda.synchronize()
+    ref, cu_ref, _, _ = oracle.pack_attend_unpack(w.q, w.k, w.v, w.mask, w.dtype)
+    err = max_err(f64(o), ref)
+    _say(f"   fused max abs err {err:.3e}")
+    assert err <= TOL[w.dtype]
+    assert (bits(o)[w.mask == 0] == 0).all()
+    T = int(cu_ref[-1])
+    ref_pk = ref.reshape(-1, H, w.d)[oracle.kept_index(w.mask)]
+    assert max_err(f64(o2[:T]), ref_pk) <= TOL[w.dtype]
+
+
 def test_explicit_scale(device):
     rva = _rva()
     w = _get("deit_b_224_p80")
