@@ -219,8 +219,8 @@ struct FragLanes16 {
   uint32_t v[4];  // V^T: row 4 g + r16 / 4, piece 2 db + (r16 & 3) / 2, half (r16 & 1)
 };
 
-__device__ __forceinline__ FragLanes16 frag_lanes16() {
-  const int lane = lane_id(), g = lane >> 4, r16 = lane & 15;
+__device__ __forceinline__ FragLanes16 frag_lanes16(int lane = lane_id()) {
+  const int g = lane >> 4, r16 = lane & 15;
   FragLanes16 L;
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) L.k[ks] = (uint32_t)kvswz(r16, ks * 4 + g);
@@ -497,7 +497,11 @@ __device__ __forceinline__ void attend_seq16(const AttnParams& p, int n, unsigne
 constexpr int kUnitsPerWave = kResidentMax16 / kQBlock / (kAttnThreads16 / 64);
 constexpr int kQSlots = 3;
 
-template <int DT, typename RowOff, typename Hook>
+// LANES_PER_TILE: recompute the fragment lane offsets at every tile (behind
+// an opaque move, so they are not hoisted) instead of holding them across
+// the tile loops; for callers whose own live state leaves no registers for
+// them, where they would otherwise be spilled and reloaded every tile.
+template <int DT, bool LANES_PER_TILE = false, typename RowOff, typename Hook>
 __device__ __forceinline__ void attend_resident16(int n, int nh, float c, unsigned char* kvbase,
                                                   Rsrc rq, Rsrc rk, Rsrc rv, Rsrc ro, RowOff roff,
                                                   Hook last_use) {
@@ -540,7 +544,16 @@ __device__ __forceinline__ void attend_resident16(int n, int nh, float c, unsign
   __syncthreads();
   last_use();
   const int ntile = (n + kKeyTile - 1) / kKeyTile;
-  const FragLanes16 lanes = frag_lanes16();
+  auto lanes_now = [&]() -> FragLanes16 {
+    if constexpr (LANES_PER_TILE) {
+      int l = lane_id();
+      asm volatile("" : "+v"(l));
+      return frag_lanes16(l);
+    } else {
+      return frag_lanes16();
+    }
+  };
+  const FragLanes16 lanes0 = frag_lanes16();
 #pragma unroll
   for (int i = 0; i < kUnitsPerWave; ++i) {
     const int u = w + i * kWaves;
@@ -561,9 +574,10 @@ __device__ __forceinline__ void attend_resident16(int n, int nh, float c, unsign
     // tile with 16 staged rows reads its K rows 16..31 from the head's
     // first V rows (their scores are masked) and skips their V rows.
     V8 kf[2][2];
-    k_frag16<DT>(Ks, 0, lanes, kf);
+    k_frag16<DT>(Ks, 0, LANES_PER_TILE ? lanes_now() : lanes0, kf);
     for (int t = 0; t < ntile; ++t) {
       const int k0 = t * kKeyTile;
+      const FragLanes16 lanes = LANES_PER_TILE ? lanes_now() : lanes0;
       V8 vf[4];
       v_frag16<DT>(Vs, k0, lanes, k0 + kQBlock < rows, vf);
       f32x4 s0, s1;
@@ -963,9 +977,9 @@ __global__ __launch_bounds__(kAttnThreads16, 3) void attend16_persistent_kernel(
       const uint32_t bytes = (uint32_t)N * rs * ES;
       auto roff = [=](int r) -> uint32_t { return (uint32_t)idx[min(r, n - 1)] * (rs * ES); };
       if (n <= p.rc)
-        attend_resident16<DT>(n, 1, p.scale_log2e, kvbase, make_rsrc(pl.q, bytes),
-                              make_rsrc(pl.k, bytes), make_rsrc(pl.v, bytes),
-                              make_rsrc(pl.o, bytes), roff, next_ready);
+        attend_resident16<DT, true>(n, 1, p.scale_log2e, kvbase, make_rsrc(pl.q, bytes),
+                                    make_rsrc(pl.k, bytes), make_rsrc(pl.v, bytes),
+                                    make_rsrc(pl.o, bytes), roff, next_ready);
       else
         attend_seq16<DT>(pl, n, kvbase, make_rsrc(pl.q, bytes), make_rsrc(pl.k, bytes),
                          make_rsrc(pl.v, bytes), make_rsrc(pl.o, bytes), roff, next_ready);
