@@ -118,12 +118,22 @@ def _check(status: int, where: str):
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    # a plain int: ctypes passes it as void* (None as NULL)
+    return None if t is None else t.data_ptr()
+
+
+# The current stream's raw handle without building a Stream object (which
+# costs about 3 us a call); the library launches on the current device.
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+_cur_device = getattr(torch._C, "_cuda_getDevice", None)
 
 
 def _stream(stream=None):
-    s = stream if stream is not None else torch.cuda.current_stream()
-    return ctypes.c_void_p(s.cuda_stream)
+    if stream is not None:
+        return stream.cuda_stream
+    if _raw_stream is not None and _cur_device is not None:
+        return _raw_stream(_cur_device())
+    return torch.cuda.current_stream().cuda_stream
 
 
 def dtype_code(t: torch.Tensor) -> int:
