@@ -248,6 +248,35 @@ def test_deterministic(device):
     assert np.array_equal(bits(a), bits(b))
 
 
+def test_runs_on_the_callers_stream(device):
+    """The launch goes to the current stream (a side stream entered with
+    torch.cuda.stream) or to an explicit stream argument: work queued on
+    that stream before the call (a fill of the inputs) is seen, and the
+    default stream need not be synchronised."""
+    rva = _rva()
+    w = _get("deit_b_224_p50")
+    q, k, v, mask = upload(w, device)
+    ref = rva.fused(q, k, v, mask)
+    torch.cuda.synchronize()
+    for explicit in (False, True):
+        side = torch.cuda.Stream()
+        q2, k2, v2 = (torch.empty_like(t) for t in (q, k, v))
+        o = torch.full_like(q, float("nan"))
+        torch.cuda.synchronize()
+        with torch.cuda.stream(side):
+            # inputs written on the side stream just before the call
+            q2.copy_(q)
+            k2.copy_(k)
+            v2.copy_(v)
+            if explicit:
+                rva.fused(q2, k2, v2, mask, out=o, stream=side)
+        if not explicit:
+            with torch.cuda.stream(side):
+                rva.fused(q2, k2, v2, mask, out=o)
+        side.synchronize()
+        assert np.array_equal(bits(o), bits(ref)), explicit
+
+
 def test_independent_images(device):
     """Perturbing one image leaves every other image's output bitwise equal."""
     rva = _rva()
