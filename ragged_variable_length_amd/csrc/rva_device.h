@@ -25,12 +25,6 @@ __device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 
-__device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-
 __device__ __forceinline__ int wave_max(int v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o));
