@@ -341,6 +341,47 @@ __device__ __forceinline__ void block_step16(const KVFrag16<DT>& f,
   prob_step16<DT>(f.vf, s0, s1, o, m, kvalid, c);
 }
 
+// Scores of keys >= kvalid (only a sequence's last tile has any) to -inf.
+__device__ __forceinline__ void mask_keys(f32x4& s0, f32x4& s1, int kvalid) {
+  if (kvalid >= kKeyTile) return;
+  const int g = lane_id() >> 4;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (4 * g + j >= kvalid) s0[j] = -INFINITY;
+    if (16 + 4 * g + j >= kvalid) s1[j] = -INFINITY;
+  }
+}
+
+// Headroom (log2 units) of the whole-sequence form's fixed reference max:
+// probabilities stay below 2^15, inside the fp16 range.
+constexpr float kRefHeadroom = 15.0f;
+
+// Probabilities of one tile against a fixed reference max m (scaled by c,
+// shared by the four lanes of a query): p = exp2(s c - m), rounded to the
+// 16-bit type, accumulated into O^T (o[0..3]) and into the row sums (o[4],
+// from an all-ones operand).  FIRST starts the accumulators from zero.
+template <int DT, bool FIRST>
+__device__ __forceinline__ void fixed_step16(const typename Half16<DT>::V8 (&vf)[4],
+                                             const f32x4& s0, const f32x4& s1, f32x4 (&o)[5],
+                                             float m, float c) {
+  typedef Half16<DT> Tr;
+  typedef typename Tr::T T;
+  typedef typename Tr::V8 V8;
+  V8 pf;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    pf[j] = (T)fast_exp2(fmaf(s0[j], c, -m));
+    pf[4 + j] = (T)fast_exp2(fmaf(s1[j], c, -m));
+  }
+  V8 ones;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) ones[j] = (T)1.0f;
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int db = 0; db < 4; ++db) o[db] = Tr::mfma(vf[db], pf, FIRST ? z : o[db]);
+  o[4] = Tr::mfma(ones, pf, FIRST ? z : o[4]);
+}
+
 // Normalise one finished query block and store its rows: O^T block db,
 // lane (r16, g) holds O[q][16 db + 4 g .. + 3]; o[4] holds the query's
 // probability sum in every element.  Rows at kOOB are dropped.
@@ -563,19 +604,35 @@ __device__ __forceinline__ void attend_resident16(int n, int nh, float c, unsign
     const int hu = u / nqb;
     const unsigned char* Ks = kvbase + hu * rows * 2 * kHeadBytes;
     const unsigned char* Vs = Ks + rows * kHeadBytes;
+    // The block's softmax runs against a fixed reference max: the first
+    // tile sets it to that tile's row max, and later tiles are only checked
+    // against it (lane-locally, no cross-lane reduction) with kRefHeadroom
+    // to spare.  The tile loop then carries no rescale of the accumulators
+    // (whose branch would cost register copies every tile).  A block whose
+    // check fails, a later score far above the first tile's, is computed
+    // again from scratch against its exact row max (rare).
+    // Every tile loop reads the next tile's K fragments right after the
+    // current tile's score products issue.  Every read stays inside the
+    // head's staged rows: a last tile with 16 staged rows reads its K rows
+    // 16..31 from the head's first V rows (their scores are masked) and
+    // skips their V rows.
     f32x4 o[5];
-#pragma unroll
-    for (int db = 0; db < 5; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m = -INFINITY;
-    // Software-pipelined over the tiles: the next tile's K fragments are
-    // read right after this tile's score products issue, so their LDS
-    // latency hides behind the softmax instead of stalling the next
-    // products.  Every read stays inside the head's staged rows: a last
-    // tile with 16 staged rows reads its K rows 16..31 from the head's
-    // first V rows (their scores are masked) and skips their V rows.
     V8 kf[2][2];
-    k_frag16<DT>(Ks, 0, LANES_PER_TILE ? lanes_now() : lanes0, kf);
-    for (int t = 0; t < ntile; ++t) {
+    float m;
+    bool redo = false;
+    {
+      const FragLanes16 lanes = LANES_PER_TILE ? lanes_now() : lanes0;
+      k_frag16<DT>(Ks, 0, lanes, kf);
+      V8 vf[4];
+      v_frag16<DT>(Vs, 0, lanes, kQBlock < rows, vf);
+      f32x4 s0, s1;
+      scores16<DT>(kf, qf[slot], s0, s1);
+      if (ntile > 1) k_frag16<DT>(Ks, kKeyTile, lanes, kf);
+      mask_keys(s0, s1, n);
+      m = quad_max(max8(s0, s1)) * c;
+      fixed_step16<DT, true>(vf, s0, s1, o, m, c);
+    }
+    for (int t = 1; t < ntile; ++t) {
       const int k0 = t * kKeyTile;
       const FragLanes16 lanes = LANES_PER_TILE ? lanes_now() : lanes0;
       V8 vf[4];
@@ -583,7 +640,40 @@ __device__ __forceinline__ void attend_resident16(int n, int nh, float c, unsign
       f32x4 s0, s1;
       scores16<DT>(kf, qf[slot], s0, s1);
       if (t + 1 < ntile) k_frag16<DT>(Ks, k0 + kKeyTile, lanes, kf);
-      prob_step16<DT>(vf, s0, s1, o, m, min(kKeyTile, n - k0), c);
+      mask_keys(s0, s1, n - k0);
+      if (__any(max8(s0, s1) * c > m + kRefHeadroom)) {
+        redo = true;
+        break;
+      }
+      fixed_step16<DT, false>(vf, s0, s1, o, m, c);
+    }
+    if (redo) {
+      float mx = -INFINITY;
+      k_frag16<DT>(Ks, 0, LANES_PER_TILE ? lanes_now() : lanes0, kf);
+      for (int t = 0; t < ntile; ++t) {
+        const FragLanes16 lanes = LANES_PER_TILE ? lanes_now() : lanes0;
+        f32x4 s0, s1;
+        scores16<DT>(kf, qf[slot], s0, s1);
+        if (t + 1 < ntile) k_frag16<DT>(Ks, (t + 1) * kKeyTile, lanes, kf);
+        mask_keys(s0, s1, n - t * kKeyTile);
+        mx = fmaxf(mx, max8(s0, s1));
+      }
+      m = quad_max(mx) * c;
+      k_frag16<DT>(Ks, 0, LANES_PER_TILE ? lanes_now() : lanes0, kf);
+      for (int t = 0; t < ntile; ++t) {
+        const int k0 = t * kKeyTile;
+        const FragLanes16 lanes = LANES_PER_TILE ? lanes_now() : lanes0;
+        V8 vf[4];
+        v_frag16<DT>(Vs, k0, lanes, k0 + kQBlock < rows, vf);
+        f32x4 s0, s1;
+        scores16<DT>(kf, qf[slot], s0, s1);
+        if (t + 1 < ntile) k_frag16<DT>(Ks, k0 + kKeyTile, lanes, kf);
+        mask_keys(s0, s1, n - k0);
+        if (t == 0)
+          fixed_step16<DT, true>(vf, s0, s1, o, m, c);
+        else
+          fixed_step16<DT, false>(vf, s0, s1, o, m, c);
+      }
     }
     store_block16<DT>(o, ro, qoff[i]);
   }

@@ -248,6 +248,43 @@ def test_deterministic(device):
     assert np.array_equal(bits(a), bits(b))
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_late_dominant_key(device, dtype):
+    """Scores in a later key tile far above every score of the first tile
+    (queries aligned with one late key and scaled up): the whole-sequence
+    form's reference max from the first tile is exceeded by much more than
+    its headroom, so those query blocks are computed again against their
+    exact max.  Fused and packed forms against the oracle."""
+    rva = _rva()
+    B, N, H = 6, 197, 2
+    counts = [197, 150, 100, 70, 40, 33]
+    w = W.random_workload(41 if dtype == "f16" else 42, B=B, N=N, H=H, dtype=dtype,
+                          counts=counts, name=f"late_key_{dtype}")
+    q = oracle.decode(w.q, dtype)
+    k = oracle.decode(w.k, dtype)
+    for b in range(B):
+        keep = np.flatnonzero(w.mask[b])
+        late = keep[-1]  # the last kept key lies in the sequence's last tile
+        for h in range(H):
+            kv = k[b, late, h]
+            # every query of the image points at that key, 3x its length
+            q[b, :, h] = 3.0 * kv / np.linalg.norm(kv) * 8.0
+    w.q = W._cast(q.astype(np.float32), dtype)
+    qd, kd, vd, md = upload(w, device)
+    o = rva.fused(qd, kd, vd, md)
+    pk = rva.pack(qd, kd, vd, md)
+    o2 = rva.ragged_attend(pk["q"], pk["k"], pk["v"], pk["cu_seqlens"], N)
+    torch.cuda.synchronize()
+    ref, cu_ref, _, _ = oracle.pack_attend_unpack(w.q, w.k, w.v, w.mask, w.dtype)
+    assert np.isfinite(f64(o)).all()
+    err = max_err(f64(o), ref)
+    _say(f"[late key] {dtype} max abs err {err:.3e}")
+    assert err <= TOL[w.dtype]
+    T = int(cu_ref[-1])
+    ref_pk = ref.reshape(-1, H, w.d)[oracle.kept_index(w.mask)]
+    assert max_err(f64(o2[:T]), ref_pk) <= TOL[w.dtype]
+
+
 def test_runs_on_the_callers_stream(device):
     """The launch goes to the current stream (a side stream entered with
     torch.cuda.stream) or to an explicit stream argument: work queued on
