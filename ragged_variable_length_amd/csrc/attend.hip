@@ -391,7 +391,8 @@ __device__ __forceinline__ void store_block16(const f32x4 (&o)[5], Rsrc ro, uint
   typedef typename Tr::T T;
   typedef typename Tr::V4 V4;
   const int g = lane_id() >> 4;
-  const float inv = 1.f / o[4][0];
+  // hardware reciprocal (about 1 ulp): ample for 16-bit outputs
+  const float inv = __builtin_amdgcn_rcpf(o[4][0]);
 #pragma unroll
   for (int db = 0; db < 4; ++db) {
     V4 out;
