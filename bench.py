@@ -1,7 +1,7 @@
 """Benchmark of the pack -> ragged attention -> unpack path on one MI355X.
 
-Headline (the JSON line's `value`): kept tokens per second of the captured
-fused launch (one graph launch = one whole pass of the path: counts and
+Headline (the JSON line's `value`): kept tokens per second of the direct
+fused launch (one kernel launch = one whole pass of the path: counts and
 offsets, row gather, attention, unpack with zero fill) on the peak-throughput
 mixed batch -- 1024 DeiT-B-shaped images, 197 tokens, 12 heads, head_dim 64,
 fp16, per-image pruning rate uniform in [0, 0.9].  Inputs are resident in
