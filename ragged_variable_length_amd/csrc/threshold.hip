@@ -22,9 +22,9 @@
 // time with coalesced 16-byte loads (8 lanes per row segment), parks the
 // 8 KB tile in LDS (16-byte pieces XOR-swizzled by row so that the eight
 // lanes of a read phase hit distinct banks) and each lane then walks its
-// own row segment.  The next tile's loads are in flight while the current
-// one is summed.  After a barrier the image's squared norms sit in LDS and
-// every thread ranks one patch against all the others.
+// own row segment.  The next two tiles' loads are in flight while the
+// current one is summed.  After a barrier the image's squared norms sit in
+// LDS and every thread ranks one patch against all the others.
 #include "rva_device.h"
 #include "rva_internal.h"
 
@@ -83,24 +83,35 @@ __global__ __launch_bounds__(1024) void threshold_l2_kernel(ThreshParams p) {
     return (r < N && cb < row_bytes) ? (uint32_t)r * row_bytes + cb : kOOB;
   };
 
-  u32x4 v[8];
-#pragma unroll
-  for (int u = 0; u < 8; ++u) v[u] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)offset(0, u), 0, 0);
-  double acc = 0.0;
-  for (int k = 0; k < nchunks; ++k) {
+  // Two tiles in flight per wave: tile k is parked and summed while tiles
+  // k + 1 and k + 2 load.  A wave reads back only the tile it wrote, and LDS
+  // executes one wave's instructions in issue order, so the exchange needs
+  // no workgroup barrier, only a compiler barrier that keeps the LDS
+  // accesses in program order; the waves of the image run independently.
+  auto step = [&](u32x4 (&v)[8], int k, double& acc) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int r = lr + 8 * u;
       *reinterpret_cast<u32x4*>(tile + r * kTileRowBytes + ((pc ^ (r & 7)) << 4)) = v[u];
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)offset(k + 1, u), 0, 0);
-    __syncthreads();
+    for (int u = 0; u < 8; ++u) v[u] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)offset(k + 2, u), 0, 0);
+    asm volatile("" ::: "memory");
     // zero pieces (past the row's end) add exact zeros
 #pragma unroll
     for (int q = 0; q < 8; ++q)
       add_squares<DT>(acc, *reinterpret_cast<const u32x4*>(tile + lane * kTileRowBytes + ((q ^ (lane & 7)) << 4)));
-    __syncthreads();
+    asm volatile("" ::: "memory");
+  };
+  u32x4 va[8], vb[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) va[u] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)offset(0, u), 0, 0);
+#pragma unroll
+  for (int u = 0; u < 8; ++u) vb[u] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)offset(1, u), 0, 0);
+  double acc = 0.0;
+  for (int k = 0; k < nchunks; k += 2) {
+    step(va, k, acc);
+    if (k + 1 < nchunks) step(vb, k + 1, acc);
   }
   if (row0 + lane < N) sq[row0 + lane] = acc;
   __syncthreads();
