@@ -352,9 +352,12 @@ __device__ __forceinline__ void mask_keys(f32x4& s0, f32x4& s1, int kvalid) {
   }
 }
 
-// Headroom (log2 units) of the whole-sequence form's fixed reference max:
-// probabilities stay below 2^15, inside the fp16 range.
-constexpr float kRefHeadroom = 15.0f;
+// Largest probability row sum the whole-sequence form's fixed reference max
+// accepts for a query block.  Probabilities are non-negative, so every one
+// of them is then at most 2^20 as well; an fp16 probability that overflowed
+// (2^16 and above round to infinity) makes the sum infinite and fails the
+// test, so every accepted fp16 probability is finite.
+constexpr float kRefSumLimit = 1048576.0f;  // 2^20
 
 // Probabilities of one tile against a fixed reference max m (scaled by c,
 // shared by the four lanes of a query): p = exp2(s c - m), rounded to the
@@ -606,12 +609,13 @@ __device__ __forceinline__ void attend_resident16(int n, int nh, float c, unsign
     const unsigned char* Ks = kvbase + hu * rows * 2 * kHeadBytes;
     const unsigned char* Vs = Ks + rows * kHeadBytes;
     // The block's softmax runs against a fixed reference max: the first
-    // tile sets it to that tile's row max, and later tiles are only checked
-    // against it (lane-locally, no cross-lane reduction) with kRefHeadroom
-    // to spare.  The tile loop then carries no rescale of the accumulators
-    // (whose branch would cost register copies every tile).  A block whose
-    // check fails, a later score far above the first tile's, is computed
-    // again from scratch against its exact row max (rare).
+    // tile sets it to that tile's row max, and later tiles use it as it is.
+    // The tile loop then carries no rescale of the accumulators (whose
+    // branch would cost register copies every tile) and no per-tile check:
+    // once the block is done, its probability row sums (o[4], from the
+    // matrix cores) must stay at or below kRefSumLimit.  A block that fails,
+    // some later score far above the first tile's, is computed again from
+    // scratch against its exact row max (rare).
     // Every tile loop reads the next tile's K fragments right after the
     // current tile's score products issue.  Every read stays inside the
     // head's staged rows: a last tile with 16 staged rows reads its K rows
@@ -620,7 +624,6 @@ __device__ __forceinline__ void attend_resident16(int n, int nh, float c, unsign
     f32x4 o[5];
     V8 kf[2][2];
     float m;
-    bool redo = false;
     {
       const FragLanes16 lanes = LANES_PER_TILE ? lanes_now() : lanes0;
       k_frag16<DT>(Ks, 0, lanes, kf);
@@ -633,7 +636,11 @@ __device__ __forceinline__ void attend_resident16(int n, int nh, float c, unsign
       m = quad_max(max8(s0, s1)) * c;
       fixed_step16<DT, true>(vf, s0, s1, o, m, c);
     }
-    for (int t = 1; t < ntile; ++t) {
+    // unrolled over the at most kResidentMax16 / kKeyTile tiles, so that a
+    // tile's offset in the staging area is a constant of the LDS reads
+#pragma unroll
+    for (int t = 1; t < kResidentMax16 / kKeyTile; ++t) {
+      if (t >= ntile) break;
       const int k0 = t * kKeyTile;
       const FragLanes16 lanes = LANES_PER_TILE ? lanes_now() : lanes0;
       V8 vf[4];
@@ -642,13 +649,9 @@ __device__ __forceinline__ void attend_resident16(int n, int nh, float c, unsign
       scores16<DT>(kf, qf[slot], s0, s1);
       if (t + 1 < ntile) k_frag16<DT>(Ks, k0 + kKeyTile, lanes, kf);
       mask_keys(s0, s1, n - k0);
-      if (__any(max8(s0, s1) * c > m + kRefHeadroom)) {
-        redo = true;
-        break;
-      }
       fixed_step16<DT, false>(vf, s0, s1, o, m, c);
     }
-    if (redo) {
+    if (__any(!(o[4][0] <= kRefSumLimit))) {
       float mx = -INFINITY;
       k_frag16<DT>(Ks, 0, LANES_PER_TILE ? lanes_now() : lanes0, kf);
       for (int t = 0; t < ntile; ++t) {
