@@ -214,6 +214,36 @@ def test_resident_boundaries(device, dtype):
     assert max_err(f64(o2[:T]), ref_pk) <= TOL[w.dtype]
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_every_length(device, dtype):
+    """Every kept count from 0 to 224, four images each (900 images, 3
+    heads, so the fused form pairs heads and ends on single-head
+    workgroups): every exit of the whole-sequence tile loop, every ragged
+    tail, and the chunked form past 208 rows.  Fused and packed forms
+    against the oracle, every row."""
+    rva = _rva()
+    N, H = 224, 3
+    counts = [n for n in range(N + 1) for _ in range(4)]
+    B = len(counts)
+    w = W.random_workload(33 if dtype == "f16" else 34, B=B, N=N, H=H, dtype=dtype,
+                          counts=counts, name=f"every_length_{dtype}")
+    _say(f"[every length] {dtype} B={B} N={N} H={H}")
+    q, k, v, mask = upload(w, device)
+    o = torch.full_like(q, float("nan"))
+    rva.fused(q, k, v, mask, out=o, max_seqlen_hint=N)
+    pk = rva.pack(q, k, v, mask)
+    o2 = rva.ragged_attend(pk["q"], pk["k"], pk["v"], pk["cu_seqlens"], N)
+    torch.cuda.synchronize()
+    ref, cu_ref, _, _ = oracle.pack_attend_unpack(w.q, w.k, w.v, w.mask, w.dtype)
+    err = max_err(f64(o), ref)
+    _say(f"   fused max abs err {err:.3e}")
+    assert err <= TOL[w.dtype]
+    assert (bits(o)[w.mask == 0] == 0).all()
+    T = int(cu_ref[-1])
+    ref_pk = ref.reshape(-1, H, w.d)[oracle.kept_index(w.mask)]
+    assert max_err(f64(o2[:T]), ref_pk) <= TOL[w.dtype]
+
+
 def test_explicit_scale(device):
     rva = _rva()
     w = _get("deit_b_224_p80")
