@@ -128,9 +128,10 @@ int rva_fused(const void* q_pad, const void* k_pad, const void* v_pad, const uin
 
 /*
  * rva_fused_persistent -- rva_fused as a persistent grid: as many workgroups
- * as stay resident, each pulling (image, head) items from a device counter,
- * fetching the next item's mask row while it works on the current one.
- * Same arguments and results as rva_fused (16-bit inputs; fp32 falls back to
+ * as stay resident, each pulling rva_fused's work items (an image's head
+ * pair, or one head of a tail image) from a device counter, one item ahead,
+ * and running them with rva_fused's per-item code.  Same arguments and
+ * results as rva_fused, bit for bit (16-bit inputs; fp32 falls back to
  * rva_fused), plus:
  *   work : int32[2] device scratch, all zero before the first call.  Every
  *          call leaves it zero again when it completes, so one buffer serves

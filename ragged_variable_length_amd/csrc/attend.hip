@@ -860,19 +860,16 @@ __device__ __forceinline__ AttnParams rebase(const AttnParams& p, size_t elem0, 
   return r;
 }
 
-template <int DT, bool FUSED>
-__device__ __forceinline__ void attend_body(const AttnParams& p, unsigned char* smem) {
+// The work of grid position `bid` of the attention launch: in the fused
+// form an image's head group (or one head of a tail image), in the packed
+// form one (sequence, head).  `hook()` is called by every thread at least
+// once after the item's first staging barrier, or after its zero fill when
+// the image keeps no token (the persistent form hands over its next item
+// index there).
+template <int DT, bool FUSED, bool LANES_PER_TILE = false, typename Hook>
+__device__ __forceinline__ void attend_item(const AttnParams& p, int bid, unsigned char* smem,
+                                            Hook hook) {
   constexpr int NT = DT == 0 ? kAttnThreads32 : kAttnThreads16;
-  int bid = blockIdx.x;
-  if constexpr (FUSED) {
-    if (p.cu_out || p.max_out) {
-      if (bid == 0) {
-        count_scan_block<NT>(p.mask, p.B, p.N, p.cu_out, p.max_out, reinterpret_cast<int*>(smem));
-        return;
-      }
-      --bid;
-    }
-  }
   // fused 16-bit: a workgroup may take several heads of one image in turn,
   // so that the mask row is read and compacted once for all of them; the
   // last tail_b images of the batch (dispatched last) take one head per
@@ -915,9 +912,9 @@ __device__ __forceinline__ void attend_body(const AttnParams& p, unsigned char* 
           const AttnParams pl = rebase(p, ((size_t)b * N * H + h) * kHeadDim, ES);
           for (int j = 0; j < nh; ++j)
             zero_pruned<NT, ES>(static_cast<char*>(pl.o) + j * kHeadDim * ES, ballots, N, H);
-          attend_resident16<DT>(n, nh, p.scale_log2e, kvbase, make_rsrc(pl.q, bytes),
+          attend_resident16<DT, LANES_PER_TILE>(n, nh, p.scale_log2e, kvbase, make_rsrc(pl.q, bytes),
                                 make_rsrc(pl.k, bytes), make_rsrc(pl.v, bytes),
-                                make_rsrc(pl.o, bytes), roff, [] {});
+                                make_rsrc(pl.o, bytes), roff, hook);
           h += nh;
         }
         return;
@@ -934,9 +931,10 @@ __device__ __forceinline__ void attend_body(const AttnParams& p, unsigned char* 
       } else {
         auto roff = [=](int r) -> uint32_t { return (uint32_t)idx[min(r, n - 1)] * (rs * ES); };
         attend_seq16<DT>(pl, n, kvbase, make_rsrc(pl.q, bytes), make_rsrc(pl.k, bytes),
-                         make_rsrc(pl.v, bytes), make_rsrc(pl.o, bytes), roff, [] {});
+                         make_rsrc(pl.v, bytes), make_rsrc(pl.o, bytes), roff, hook);
       }
     }
+    if (n <= 0) hook();
   } else {
     const int h = hg;
     const int row0 = p.cu[b];
@@ -952,12 +950,28 @@ __device__ __forceinline__ void attend_body(const AttnParams& p, unsigned char* 
       if (n <= p.rc)
         attend_resident16<DT>(n, 1, p.scale_log2e, smem, make_rsrc(pl.q, bytes),
                               make_rsrc(pl.k, bytes), make_rsrc(pl.v, bytes),
-                              make_rsrc(pl.o, bytes), roff, [] {});
+                              make_rsrc(pl.o, bytes), roff, hook);
       else
         attend_seq16<DT>(pl, n, smem, make_rsrc(pl.q, bytes), make_rsrc(pl.k, bytes),
-                         make_rsrc(pl.v, bytes), make_rsrc(pl.o, bytes), roff, [] {});
+                         make_rsrc(pl.v, bytes), make_rsrc(pl.o, bytes), roff, hook);
     }
   }
+}
+
+template <int DT, bool FUSED>
+__device__ __forceinline__ void attend_body(const AttnParams& p, unsigned char* smem) {
+  constexpr int NT = DT == 0 ? kAttnThreads32 : kAttnThreads16;
+  int bid = blockIdx.x;
+  if constexpr (FUSED) {
+    if (p.cu_out || p.max_out) {
+      if (bid == 0) {
+        count_scan_block<NT>(p.mask, p.B, p.N, p.cu_out, p.max_out, reinterpret_cast<int*>(smem));
+        return;
+      }
+      --bid;
+    }
+  }
+  attend_item<DT, FUSED>(p, bid, smem, [] {});
 }
 
 // 16-bit: 4 waves, register budget for 3 waves per SIMD (3 workgroups per CU).
@@ -973,122 +987,50 @@ __global__ __launch_bounds__(kAttnThreads32) void attend32_kernel(AttnParams p) 
   attend_body<0, FUSED>(p, smem);
 }
 
-// Persistent form of the fused 16-bit kernel.  A grid of resident
-// workgroups pulls (image, head) items from a device counter instead of
-// being dispatched one item each.  That removes the dispatch gap between
-// items, and it takes the mask round trip off the critical path: while item
-// i runs, the workgroup already holds the index of item i + 1 (fetched one
-// item ahead), pulls its mask row into LDS with direct-to-LDS loads, and
-// compacts it as soon as item i no longer reads its own kept-row list
-// (before item i's multiply).  At the item boundary the next item's loads
-// issue at once.  The workgroup that leaves last returns the counter to
-// zero for the next launch.
+// Persistent form of the fused 16-bit kernel: as many workgroups as stay
+// resident, each pulling items from a device counter instead of being
+// dispatched one item each.  The items are exactly the one-launch kernel's
+// grid positions (an image's head pair, or one head of a tail image) and
+// run the same per-item code, so registers, staging and results are the
+// same bit for bit; what changes is that no workgroup launch separates two
+// items of one slot.  Thread 0 fetches the next item's index while the
+// current item runs (one atomic ahead) and hands it to the workgroup through
+// a 4-byte LDS slot past the staging area: it writes the slot right after
+// the item's first staging barrier, where its wave has already waited for
+// every earlier load, the atomic included.  The workgroup that leaves last
+// returns the counter to zero for the next launch.
 // A workgroup barrier that orders LDS only: this wave's LDS accesses
-// complete, then s_barrier; no wait for global memory.  The clobber keeps the
+// complete, then s_barrier; no wait for global memory, so the item boundary
+// does not wait for the item's output stores.  The clobber keeps the
 // compiler from moving memory accesses across it.
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-constexpr int kMaskWindow = 2048;  // LDS bytes for one mask row (N + 3 <= 1027, whole dwords)
-constexpr int kPersistentStaticLds = kMaskWindow + 256;
-
 template <int DT>
 __global__ __launch_bounds__(kAttnThreads16, 3) void attend16_persistent_kernel(AttnParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
-  __shared__ __align__(16) unsigned char s_mask[kMaskWindow];  // its own LDS object, see below
-  __shared__ int s_item;
   constexpr int NT = kAttnThreads16;
-  constexpr int PER = compact_per<NT>();
-  constexpr int ES = 2;
-  const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
-  const int H = p.H, N = p.N, G = p.B * p.H;
+  const int tid = threadIdx.x;
+  int* slot = reinterpret_cast<int*>(smem + p.item_slot);
+  const int HG = p.heads_per_wg;
+  const int nitems = (p.B - p.tail_b) * ((p.H + HG - 1) / HG) + p.tail_b * p.H;
   if (blockIdx.x == 0 && (p.cu_out || p.max_out)) {
-    count_scan_block<NT>(p.mask, p.B, N, p.cu_out, p.max_out, reinterpret_cast<int*>(smem));
-    __syncthreads();
+    count_scan_block<NT>(p.mask, p.B, p.N, p.cu_out, p.max_out, reinterpret_cast<int*>(smem));
+    __syncthreads();  // its LDS is reused below
   }
-  const uint32_t mask_bytes = (uint32_t)p.B * (uint32_t)N;
-  const uint32_t mask_tail = mask_bytes & ~3u;  // bytes at or past it are read directly
-  const Rsrc rmask = make_rsrc(p.mask, mask_bytes);
-  // The mask row of `item` as whole dwords into s_mask (lane L of a load
-  // lands at byte 4 L).  s_mask is a separate LDS object so that the
-  // compiler's wait for these loads is not attached to reads of smem.
-  auto prefetch_mask = [&](int item) {
-    const uint32_t a0 = ((uint32_t)(item / H) * (uint32_t)N) & ~3u;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int dw0 = u * 256 + w * 64;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rmask, (__attribute__((address_space(3))) void*)(s_mask + dw0 * 4), 4,
-          a0 + (uint32_t)(dw0 + lane) * 4, 0, 0, 0);
-    }
-  };
-  uint16_t* idx = reinterpret_cast<uint16_t*>(smem);
-  uint64_t* ballots = reinterpret_cast<uint64_t*>(smem + attn_ballots_off(N));
-  int32_t* cnt = reinterpret_cast<int32_t*>(smem + attn_cnt_off(N));
-  unsigned char* kvbase = smem + attn_compact_bytes(N);
-  // compaction of `item` from the prefetched row (its last bytes past the
-  // final whole dword of the mask tensor straight from memory)
-  auto compact_item = [&](int item) -> int {
-    const uint32_t start = (uint32_t)(item / H) * (uint32_t)N;
-    const unsigned char* row = s_mask + (start & 3u);
-    uint8_t mb[PER];
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int j = (w + i * (NT / 64)) * 64 + lane;
-      mb[i] = 0;
-      if (j < N) mb[i] = start + (uint32_t)j < mask_tail ? row[j] : p.mask[start + j];
-    }
-    return compact_bytes<NT, uint16_t>(mb, N, idx, nullptr, ballots, cnt);
-  };
-
-  if (tid == 0) s_item = atomicAdd(p.work, 1);
+  if (tid == 0) *slot = atomicAdd(p.work, 1);
   __syncthreads();
-  int cur = s_item;
-  __syncthreads();
-  if (tid == 0) s_item = atomicAdd(p.work, 1);
-  if (cur < G) prefetch_mask(cur);
-  __syncthreads();  // (with its fence: the fetch and the prefetch have landed)
-  int nxt = s_item;
-  int n = cur < G ? compact_item(cur) : 0;
-  const uint32_t rs = (uint32_t)(H * kHeadDim);
-  while (cur < G) {
-    int pending = G;  // thread 0: index of the item after nxt
-    if (tid == 0 && nxt < G) pending = atomicAdd(p.work, 1);
-    if (nxt < G) prefetch_mask(nxt);
-    int n_next = 0;
-    // runs once all of cur's kept-row reads are done; the fetch and the
-    // prefetch were issued before cur's first staging, whose barrier (with
-    // its memory fence) has already seen them land
-    auto next_ready = [&] {
-      if (tid == 0) s_item = pending;
-      n_next = nxt < G ? compact_item(nxt) : 0;
-    };
-    const int b = cur / H, h = cur - b * H;
-    const AttnParams pl = rebase(p, ((size_t)b * N * H + h) * kHeadDim, ES);
-    zero_pruned<NT, ES>(static_cast<char*>(pl.o), ballots, N, H);
-    if (n > 0) {
-      const uint32_t bytes = (uint32_t)N * rs * ES;
-      auto roff = [=](int r) -> uint32_t { return (uint32_t)idx[min(r, n - 1)] * (rs * ES); };
-      if (n <= p.rc)
-        attend_resident16<DT, true>(n, 1, p.scale_log2e, kvbase, make_rsrc(pl.q, bytes),
-                                    make_rsrc(pl.k, bytes), make_rsrc(pl.v, bytes),
-                                    make_rsrc(pl.o, bytes), roff, next_ready);
-      else
-        attend_seq16<DT>(pl, n, kvbase, make_rsrc(pl.q, bytes), make_rsrc(pl.k, bytes),
-                         make_rsrc(pl.v, bytes), make_rsrc(pl.o, bytes), roff, next_ready);
-    } else {
-      __syncthreads();  // every wave's zero fill read the ballots; fetch and prefetch landed
-      next_ready();
-    }
-    // Item boundary: only LDS is shared across it (cur's staged rows, s_item),
-    // so the barriers wait for this wave's LDS accesses but not, as
-    // __syncthreads would, for cur's output stores still draining.
-    lds_barrier();  // every wave is done with cur's LDS and has written s_item
-    cur = nxt;
-    nxt = s_item;
-    n = n_next;
-    lds_barrier();  // s_item is read before the next iteration writes it
+  int item = *slot;
+  while (item < nitems) {
+    int next = 0;
+    if (tid == 0) next = atomicAdd(p.work, 1);
+    attend_item<DT, true, true>(p, item, smem, [&] {
+      if (tid == 0) *slot = next;
+    });
+    // every wave is done with the item's LDS and the slot holds the next index
+    lds_barrier();
+    item = *slot;
   }
   if (tid == 0) {
     __threadfence();
@@ -1102,12 +1044,13 @@ __global__ __launch_bounds__(kAttnThreads16, 3) void attend16_persistent_kernel(
 // Rows of the 16-bit staging area a launch gives whole sequences: kc when
 // the length hint is below the chunk cap; otherwise as many 16-row blocks
 // as the LDS left to each of 3 workgroups per CU holds (after the
-// compaction area and static LDS), at most kResidentMax16.  At N = 197
-// that is 208 rows: 53248 bytes of K/V and 448 of compaction area.
-static int resident_rows(int dtype, bool fused, int N, int kc, int static_bytes) {
+// compaction area and `reserved` bytes), at most kResidentMax16.  At
+// N = 197 that is 208 rows: 53248 bytes of K/V, 448 of compaction area and
+// the 16-byte item slot.
+static int resident_rows(int dtype, bool fused, int N, int kc, int reserved) {
   if (dtype == 0) return 0;
   if (kc < kKcMax16) return kc;
-  const long long per_wg = (long long)kLdsPerWg16 - static_bytes -
+  const long long per_wg = (long long)kLdsPerWg16 - reserved -
                            (fused ? (long long)attn_compact_bytes(N) : 0);
   int rows = (int)(per_wg / (kHeadDim * 2 * 2)) / kQBlock * kQBlock;
   if (rows > kResidentMax16) rows = kResidentMax16;
@@ -1116,17 +1059,24 @@ static int resident_rows(int dtype, bool fused, int N, int kc, int static_bytes)
 
 static int kv_rows(int dtype, int kc, int rc) { return dtype == 0 ? kc : (rc > kc ? rc : kc); }
 
+// Dynamic LDS of the fused 16-bit kernels: compaction area, staging area and
+// the persistent form's item slot (reserved by both forms, so that both give
+// the same sequences the same staging).
+static size_t fused16_lds(int N, int kc, int rc) {
+  return attn_lds_bytes(1, true, N, kv_rows(1, kc, rc)) + kItemSlotBytes;
+}
+
 int attend_persistent_per_cu(int N, int kc) {
-  const int rc = resident_rows(1, true, N, kc, kPersistentStaticLds);
-  const size_t lds = attn_lds_bytes(1, true, N, kv_rows(1, kc, rc)) + kPersistentStaticLds;
-  const int by_lds = (int)(kLdsPerCu / lds);
+  const int rc = resident_rows(1, true, N, kc, kItemSlotBytes);
+  const int by_lds = (int)(kLdsPerCu / fused16_lds(N, kc, rc));
   return by_lds < kAttnWgPerCu16 ? by_lds : kAttnWgPerCu16;  // 3 waves per SIMD by registers
 }
 
 hipError_t launch_attend_persistent(const AttnParams& p0, int dtype, int grid, hipStream_t s) {
   AttnParams p = p0;
-  p.rc = resident_rows(dtype, true, p.N, p.kc, kPersistentStaticLds);
-  const size_t lds = attn_lds_bytes(dtype, true, p.N, kv_rows(dtype, p.kc, p.rc));
+  p.rc = resident_rows(dtype, true, p.N, p.kc, kItemSlotBytes);
+  const size_t lds = fused16_lds(p.N, p.kc, p.rc);
+  p.item_slot = (int)(lds - kItemSlotBytes);
   if (dtype == 1)
     hipLaunchKernelGGL((attend16_persistent_kernel<1>), dim3(grid), dim3(kAttnThreads16), lds, s, p);
   else
@@ -1134,19 +1084,15 @@ hipError_t launch_attend_persistent(const AttnParams& p0, int dtype, int grid, h
   return hipGetLastError();
 }
 
-// Dynamic LDS limit: the 160 KB of a CU minus the kernel's static LDS.
-static hipError_t set_lds_limit(const void* fn, int static_bytes = 0) {
-  return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
-                             kLdsPerCu - static_bytes);
+// Dynamic LDS limit: the 160 KB of a CU.
+static hipError_t set_lds_limit(const void* fn) {
+  return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsPerCu);
 }
 
 hipError_t attend_init() {
-  for (const void* f : {reinterpret_cast<const void*>(&attend16_persistent_kernel<1>),
-                        reinterpret_cast<const void*>(&attend16_persistent_kernel<2>)}) {
-    hipError_t e = set_lds_limit(f, kPersistentStaticLds);
-    if (e != hipSuccess) return e;
-  }
-  const void* fns[6] = {reinterpret_cast<const void*>(&attend32_kernel<false>),
+  const void* fns[8] = {reinterpret_cast<const void*>(&attend16_persistent_kernel<1>),
+                        reinterpret_cast<const void*>(&attend16_persistent_kernel<2>),
+                        reinterpret_cast<const void*>(&attend32_kernel<false>),
                         reinterpret_cast<const void*>(&attend32_kernel<true>),
                         reinterpret_cast<const void*>(&attend16_kernel<1, false>),
                         reinterpret_cast<const void*>(&attend16_kernel<1, true>),
@@ -1161,8 +1107,10 @@ hipError_t attend_init() {
 
 hipError_t launch_attend(const AttnParams& p0, int dtype, bool fused, hipStream_t s) {
   AttnParams p = p0;
-  p.rc = resident_rows(dtype, fused, p.N, p.kc, 0);
-  const size_t lds = attn_lds_bytes(dtype, fused, p.N, kv_rows(dtype, p.kc, p.rc));
+  const bool fused16 = fused && dtype != 0;
+  p.rc = resident_rows(dtype, fused, p.N, p.kc, fused16 ? kItemSlotBytes : 0);
+  const size_t lds = fused16 ? fused16_lds(p.N, p.kc, p.rc)
+                             : attn_lds_bytes(dtype, fused, p.N, kv_rows(dtype, p.kc, p.rc));
   const int hg = (fused && dtype != 0) ? p.heads_per_wg : 1;
   const int tail = (fused && dtype != 0) ? p.tail_b : 0;
   const int grid = (p.B - tail) * ((p.H + hg - 1) / hg) + tail * p.H +

@@ -373,11 +373,36 @@ int device_cus(int* out) {
   return RVA_OK;
 }
 
-int enqueue_attend_persistent(const rva::AttnParams& p, int dtype, hipStream_t s) {
+// How the fused 16-bit form groups heads: pairs of an image's heads per
+// workgroup only when the pairs still fill every resident slot (3 per CU)
+// at least twice over; the images dispatched last (about two slot-fills of
+// single heads) stay unpaired.  Returns the number of work items (grid
+// positions, not counting the offsets workgroup).
+int group_heads(rva::AttnParams* p, int dtype, bool fused, long long* items) {
+  p->heads_per_wg = 1;
+  p->tail_b = 0;
+  if (fused && dtype != RVA_F32 && p->H > 1) {
+    int cus = 0;
+    RVA_TRY(device_cus(&cus));
+    const long long slots = 3LL * cus;
+    if ((long long)p->B * ((p->H + 1) / 2) >= 2 * slots) {
+      p->heads_per_wg = 2;
+      const long long t = (2 * slots + p->H - 1) / p->H;
+      p->tail_b = (int)(t < p->B ? t : p->B);
+    }
+  }
+  const int hg = p->heads_per_wg;
+  *items = (long long)(p->B - p->tail_b) * ((p->H + hg - 1) / hg) + (long long)p->tail_b * p->H;
+  return RVA_OK;
+}
+
+int enqueue_attend_persistent(const rva::AttnParams& p0, int dtype, hipStream_t s) {
   RVA_TRY(ensure_init());
+  rva::AttnParams p = p0;
+  long long items = 0;
+  RVA_TRY(group_heads(&p, dtype, true, &items));
   int cus = 0;
   RVA_TRY(device_cus(&cus));
-  const long long items = (long long)p.B * p.H;
   long long grid = (long long)rva::attend_persistent_per_cu(p.N, p.kc) * cus;
   if (grid > items) grid = items;
   if (grid < 1) grid = 1;
@@ -389,21 +414,8 @@ int enqueue_attend_persistent(const rva::AttnParams& p, int dtype, hipStream_t s
 int enqueue_attend(const rva::AttnParams& p0, int dtype, bool fused, hipStream_t s) {
   RVA_TRY(ensure_init());
   rva::AttnParams p = p0;
-  p.heads_per_wg = 1;
-  p.tail_b = 0;
-  if (fused && dtype != RVA_F32 && p.H > 1) {
-    // pair the heads of an image only when the pairs still fill every
-    // resident slot (3 per CU) at least twice over; the images dispatched
-    // last (about two slot-fills of single heads) stay unpaired
-    int cus = 0;
-    RVA_TRY(device_cus(&cus));
-    const long long slots = 3LL * cus;
-    if ((long long)p.B * ((p.H + 1) / 2) >= 2 * slots) {
-      p.heads_per_wg = 2;
-      const long long t = (2 * slots + p.H - 1) / p.H;
-      p.tail_b = (int)(t < p.B ? t : p.B);
-    }
-  }
+  long long items = 0;
+  RVA_TRY(group_heads(&p, dtype, fused, &items));
   hipError_t e = rva::launch_attend(p, dtype, fused, s);
   if (e != hipSuccess) return hip_fail(e, fused ? "fused launch" : "attention launch");
   return RVA_OK;

@@ -32,6 +32,7 @@ constexpr int kAttnWgPerCu16 = 3;
 constexpr int kLdsGranule = 1280;
 constexpr int kLdsPerWg16 = kLdsPerCu / kAttnWgPerCu16 / kLdsGranule * kLdsGranule;
 constexpr int kPitch32 = 68;   // floats per staged K/V row for fp32
+constexpr int kItemSlotBytes = 16;  // fused 16-bit LDS past the staging area (persistent item slot)
 
 struct AttnParams {
   const void* q;
@@ -49,6 +50,7 @@ struct AttnParams {
   int heads_per_wg;       // fused 16-bit form: heads of one image a workgroup takes in turn (>= 1)
   int rc;                 // 16-bit: longest sequence staged whole (rows, multiple of 16, >= kc); set at launch
   int tail_b;             // fused 16-bit form: last images taken one head per workgroup (0..B)
+  int item_slot;          // persistent form: byte offset of its 4-byte item slot in dynamic LDS; set at launch
 };
 
 struct CopyParams {
