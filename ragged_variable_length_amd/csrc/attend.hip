@@ -24,18 +24,22 @@
 //    product: each lane then holds one query and 4+4 keys, which is exactly
 //    the per-lane slice the second product O^T = V^T P^T takes as its B
 //    operand, so P never leaves registers;
-//  * softmax in fp32 with exp2 (log2 e folded into the scale).  The running
-//    max is shared by the four lanes of a query with two lane-swap steps;
-//    row sums come from the matrix cores (an all-ones operand times the
-//    rounded probabilities).  The output is rescaled only when
-//    the max grows by more than 2^8 (the stale max still bounds every
-//    probability by 2^8, far inside fp16/bf16 range, and cancels exactly in
-//    the final division);
+//  * softmax in fp32 with exp2 (log2 e folded into the scale); row sums come
+//    from the matrix cores (an all-ones operand times the rounded
+//    probabilities).  A sequence staged whole runs each query block against
+//    a fixed reference max, the first key tile's row max (shared by the four
+//    lanes of a query with two lane-swap steps), with no rescale and no check
+//    in the tile loop; the block is accepted when its row sums stay at or
+//    below 2^20 and computed again against its exact max otherwise.  The
+//    chunked form keeps a running max and rescales only when it grows by
+//    more than 2^8.  Either reference cancels exactly in the final division;
 //  * the fused form first compacts the image's keep-mask row in LDS, reads
 //    Q/K/V rows straight from the padded tensors through that list, writes
 //    O rows straight to padded positions and zero-fills pruned rows.  An
 //    optional extra workgroup computes cu_seqlens / max_seqlen in the same
-//    launch.
+//    launch;
+//  * the persistent form runs the fused form's items (head pairs, tail
+//    heads) in a loop over a device work counter, one resident grid.
 // fp32 inputs use the 16x16x4 fp32 matrix-core product (no precision is
 // given up) with K and V both staged in LDS and 8-wave workgroups.
 #include <math.h>
