@@ -133,3 +133,34 @@ def test_persistent_full_size(device):
             keep, rows = oracle.attend_image_head(w.q, w.k, w.v, w.mask, w.dtype, int(b), h)
             got = o2h[int(b), keep, h].double().numpy()
             assert np.abs(got - rows).max() <= TOL[w.dtype]
+
+
+def test_persistent_every_length(device):
+    """Every kept count from 0 to 224, four images each (900 images, 3 heads:
+    head pairs, single-head tail items, images with no kept token, and the
+    chunked form past 208 rows, where the next item's index is handed over
+    from inside the chunk loop).  Bits equal to the one-launch kernel, the
+    oracle on every row, and the counter back at zero."""
+    rva = _rva()
+    N, H = 224, 3
+    counts = [n for n in range(N + 1) for _ in range(4)]
+    w = W.random_workload(35, B=len(counts), N=N, H=H, dtype="bf16", counts=counts,
+                          name="persistent_every_length")
+    _say(f"[persistent] every length B={w.B} N={N} H={H}")
+    q, k, v, mask = upload(w, device)
+    work = torch.zeros(2, dtype=torch.int32, device=device)
+    o1, cu1, mx1 = _outs(q, device)
+    o2, cu2, mx2 = _outs(q, device)
+    rva.fused(q, k, v, mask, out=o1, cu_seqlens=cu1, max_seqlen=mx1, max_seqlen_hint=N)
+    for _ in range(2):
+        o2.fill_(7.0)
+        rva.fused_persistent(q, k, v, mask, work, out=o2, cu_seqlens=cu2, max_seqlen=mx2,
+                             max_seqlen_hint=N)
+        torch.cuda.synchronize()
+        _assert_same_bits(o2, o1)
+        assert np.array_equal(cu2.cpu().numpy(), cu1.cpu().numpy())
+        assert work.cpu().tolist() == [0, 0]
+    ref, cu_ref, mx_ref, _ = oracle.pack_attend_unpack(w.q, w.k, w.v, w.mask, w.dtype)
+    assert np.array_equal(cu2.cpu().numpy(), cu_ref)
+    assert int(mx2.item()) == int(mx_ref)
+    assert max_err(f64(o2), ref) <= TOL[w.dtype]
