@@ -436,7 +436,12 @@ PROFILE_COMMANDS = {
              "-d $R/gpurun_out/prof_fetch -o fused -- python3 $R/bench.py --profile",
     "write": _ROCPROF + "timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE --output-format csv "
              "-d $R/gpurun_out/prof_write -o fused -- python3 $R/bench.py --profile",
+    "util": _ROCPROF + "timeout -s KILL 90 rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_ACTIVE_INST_VALU "
+            "SQ_BUSY_CU_CYCLES SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_VALU_TRANS_F32 SQ_WAVE_CYCLES "
+            "SQ_INSTS_LDS GRBM_GUI_ACTIVE --output-format csv -d $R/gpurun_out/prof_util -o fused "
+            "-- python3 $R/bench.py --profile",
 }
+CU_NUM, SIMD_NUM, XCD_NUM = 256, 1024, 8
 
 
 def _read_csv(path):
@@ -518,6 +523,54 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, cmds):
     print(json.dumps(out))
 
 
+def summarize_util(util_dir, cmds):
+    """Matrix-core and VALU utilisation of the fused kernel from the "util"
+    counter run: MfmaUtil = MFMA busy cycles / (GUI-active cycles x SIMDs),
+    VALUBusy = VALU-active cycles / (GUI-active cycles x CUs), with the
+    GUI-active count of the busiest XCD; instruction counts per launch."""
+    import glob
+    rows = _read_csv(glob.glob(os.path.join(util_dir, "*counter_collection.csv"))[0])
+    per = {}
+    durs = {}
+    for r in rows:
+        if PROFILE_KERNEL not in r["Kernel_Name"]:
+            continue
+        per.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        durs[r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    m = {k: statistics.mean(v) for k, v in per.items()}
+    n = len(per["GRBM_GUI_ACTIVE"])
+    gui = m["GRBM_GUI_ACTIVE"] / XCD_NUM  # summed over the XCDs' GRBM instances
+    us = statistics.mean(durs.values())
+    mfma_util = 100 * m["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * SIMD_NUM)
+    valu_busy = 100 * m["SQ_ACTIVE_INST_VALU"] / CU_NUM / gui
+    import workloads as W
+    flops = workload_stats(W.mixed_peak())["flops"]
+    mfma_flops = m["SQ_INSTS_MFMA"] * 16 * 16 * 32 * 2
+    lines = ["# Fused kernel, mixed batch (1024 images, DeiT-B 224): matrix-core and VALU utilisation", "",
+             "Command (from the repository root, after building):", "",
+             "```", cmds["util"], "```", "",
+             f"Mean over {n} dispatches of `{PROFILE_KERNEL}` (counters summed over the device; "
+             f"GRBM_GUI_ACTIVE divided by the {XCD_NUM} XCDs).", "",
+             "| counter | per launch |", "|---|---|"]
+    for k in sorted(m):
+        lines.append(f"| {k} | {m[k]:,.0f} |")
+    lines += ["", "| derived | value |", "|---|---|",
+              f"| kernel duration under counters (us) | {us:.1f} |",
+              f"| GUI-active cycles per XCD | {gui:,.0f} ({gui / us / 1e3:.2f} GHz over the duration) |",
+              f"| MfmaUtil: MFMA busy / (GUI-active x {SIMD_NUM} SIMDs) | {mfma_util:.1f}% |",
+              f"| VALUBusy: VALU-active / (GUI-active x {CU_NUM} CUs) | {valu_busy:.1f}% |",
+              f"| MFMA instructions (16x16x32) | {m['SQ_INSTS_MFMA']:,.0f} |",
+              f"| matrix-core FLOPs executed / algorithmic (4 d H sum n^2 = {flops / 1e9:.1f} G) | "
+              f"{mfma_flops / flops:.2f} (padding to 16-query blocks and 32-key tiles, row sums) |",
+              f"| VALU instructions per MFMA | {m['SQ_INSTS_VALU'] / m['SQ_INSTS_MFMA']:.1f} |",
+              f"| transcendental (exp2, rcp) per MFMA | {m['SQ_INSTS_VALU_TRANS_F32'] / m['SQ_INSTS_MFMA']:.2f} |",
+              f"| LDS instructions per MFMA | {m['SQ_INSTS_LDS'] / m['SQ_INSTS_MFMA']:.2f} |", "",
+              f"Kernel source hash (attend.hip, rva_device.h, rva_internal.h): `{kernel_source_hash()}`"]
+    with open(os.path.join(ROOT, "profiles", "fused_mixed_b1024_utilisation.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -529,7 +582,12 @@ def main():
                     help="profiling target: a calibration copy, then the headline only")
     ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write the profiles/ summaries from rocprofv3 output of --profile runs")
+    ap.add_argument("--summarize-util", metavar="UTIL_DIR",
+                    help="write the profiles/ utilisation summary from the rocprofv3 counter run")
     args = ap.parse_args()
+    if args.summarize_util:
+        summarize_util(args.summarize_util, PROFILE_COMMANDS)
+        return
     if args.summarize:
         summarize_profiles(*args.summarize, PROFILE_COMMANDS)
         return
