@@ -375,7 +375,7 @@ int device_cus(int* out) {
 
 // How the fused 16-bit form groups heads: pairs of an image's heads per
 // workgroup only when the pairs still fill every resident slot (3 per CU)
-// at least twice over; the images dispatched last (about two slot-fills of
+// at least twice over; the images dispatched last (about one slot-fill of
 // single heads) stay unpaired.  Returns the number of work items (grid
 // positions, not counting the offsets workgroup).
 int group_heads(rva::AttnParams* p, int dtype, bool fused, long long* items) {
@@ -387,7 +387,7 @@ int group_heads(rva::AttnParams* p, int dtype, bool fused, long long* items) {
     const long long slots = 3LL * cus;
     if ((long long)p->B * ((p->H + 1) / 2) >= 2 * slots) {
       p->heads_per_wg = 2;
-      const long long t = (2 * slots + p->H - 1) / p->H;
+      const long long t = (slots + p->H - 1) / p->H;
       p->tail_b = (int)(t < p->B ? t : p->B);
     }
   }
