@@ -149,7 +149,9 @@ def make_plans(ctx, w, tensors, staged=True):
     mx = t.empty(1, dtype=t.int32, device=ctx.dev)
     hint = int(w.counts.max())
     plans = {"fused_graph": rva.Plan(rva.FUSED, q=q, k=k, v=v, mask=mask, out=out, cu_seqlens=cu,
-                                     max_seqlen=mx, max_seqlen_hint=hint)}
+                                     max_seqlen=mx, max_seqlen_hint=hint),
+             "fused_plan_direct": rva.Plan(rva.FUSED_DIRECT, q=q, k=k, v=v, mask=mask, out=out,
+                                           cu_seqlens=cu, max_seqlen=mx, max_seqlen_hint=hint)}
     if staged:
         packed = {nm: t.empty((B * N, H, d), dtype=q.dtype, device=ctx.dev) for nm in "qkvo"}
         plans["staged_graph"] = rva.Plan(rva.STAGED, q=q, k=k, v=v, mask=mask, out=out,
@@ -209,6 +211,11 @@ def measure_config(ctx, w, reps, floor_us):
     for name, plan in make_plans(ctx, w, tensors).items():
         res[name] = timings(ctx, plan.launch, reps)
         plan.close()
+    # the direct-launch plan: arguments validated once, one short call per launch
+    pd = res["fused_plan_direct"]
+    pd["kept_tokens_per_s"] = round(stats["T"] / (pd["latency_us"] * 1e-6))
+    pd["per_call_frac"] = round(max(direct["roofline_cold"]["t_bound_us"], floor_us) /
+                                pd["latency_us"], 4)
     # the attention kernel on its own (packed operands), cold
     rva, t = ctx.rva, ctx.torch
     q, k, v, mask = tensors
@@ -686,7 +693,7 @@ def main():
         for wk in W.all_configs():
             log(f"measuring {wk.name} ...")
             per.append(measure_config(ctx, wk, reps if wk.B < 1024 else 50,
-                                      floor["graph_latency_us"]))
+                                      floor["direct_latency_us"]))
             torch.cuda.empty_cache()
         line["per_config"] = per
         log("measuring the keep-mask ...")

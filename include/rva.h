@@ -223,6 +223,11 @@ int rva_out_projection(const void* o, const int32_t* kept_index, const int32_t* 
  *      RVA_PLAN_PERSISTENT : rva_fused_persistent (1 kernel); the plan owns
  *                        its work counter (8 bytes of device memory,
  *                        allocated and zeroed at creation, freed at destroy).
+ *      RVA_PLAN_FUSED_DIRECT : rva_fused (1 kernel) without a graph: the
+ *                        arguments are validated once at creation and each
+ *                        rva_plan_launch enqueues the kernel directly, which
+ *                        on ROCm costs less than a one-kernel graph launch.
+ *                        Nothing is captured or allocated on the device.
  * Every pointer and size is fixed at creation; the CONTENTS of the inputs
  * (including the mask) may change between launches.  Staged mode needs the
  * packed scratch buffers q/k/v/o_packed (capacity B*N rows each) and
@@ -230,14 +235,16 @@ int rva_out_projection(const void* o, const int32_t* kept_index, const int32_t* 
  * packed buffers; cu_seqlens and max_seqlen may be NULL.
  * rva_plan_create validates like the direct calls, captures on a private
  * stream and instantiates a HIP graph (host-side allocation by the runtime);
- * rva_plan_launch enqueues one graph launch on `stream`.
+ * rva_plan_launch enqueues one graph launch on `stream` (a direct kernel
+ * launch in RVA_PLAN_FUSED_DIRECT mode).
  */
 typedef enum {
   RVA_PLAN_STAGED = 0,
   RVA_PLAN_FUSED = 1,
   RVA_PLAN_EMPTY = 2,
   RVA_PLAN_L2_FUSED = 3,
-  RVA_PLAN_PERSISTENT = 4
+  RVA_PLAN_PERSISTENT = 4,
+  RVA_PLAN_FUSED_DIRECT = 5
 } rva_plan_mode;
 
 typedef struct {

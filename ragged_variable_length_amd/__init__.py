@@ -25,7 +25,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "librva.so")
 
 F32, F16, BF16 = 0, 1, 2
-STAGED, FUSED, EMPTY, L2_FUSED, PERSISTENT = 0, 1, 2, 3, 4
+STAGED, FUSED, EMPTY, L2_FUSED, PERSISTENT, FUSED_DIRECT = 0, 1, 2, 3, 4, 5
 MAX_TOKENS = 1024
 HEAD_DIM = 64
 
@@ -332,7 +332,9 @@ def empty(count: int = 1, stream=None):
 
 
 class Plan:
-    """A captured launch sequence (HIP graph) replayed with one launch.
+    """A captured launch sequence (HIP graph) replayed with one launch, or
+    (mode FUSED_DIRECT) the fused launch validated once and enqueued directly
+    by every launch().
 
     Tensors given here are kept alive by the plan; their contents may change
     between launches, their addresses may not.

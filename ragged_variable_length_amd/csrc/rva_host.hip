@@ -427,6 +427,10 @@ struct rva_plan_s {
   hipGraph_t graph;
   hipGraphExec_t exec;
   int32_t* work;  // persistent mode: the plan's own work counter (device), else NULL
+  // direct mode (no graph): the validated launch, enqueued as is
+  bool direct;
+  rva::AttnParams attn;
+  int dtype;
 };
 
 namespace {
@@ -458,7 +462,7 @@ int capture_plan(rva_plan* out, F enqueue) {
     (void)hipGraphDestroy(graph);
     return hip_fail(e, "graph instantiate");
   }
-  rva_plan_s* plan = new (std::nothrow) rva_plan_s{graph, exec, nullptr};
+  rva_plan_s* plan = new (std::nothrow) rva_plan_s{graph, exec, nullptr, false, {}, 0};
   if (!plan) {
     (void)hipGraphExecDestroy(exec);
     (void)hipGraphDestroy(graph);
@@ -589,6 +593,7 @@ int rva_plan_create(const rva_plan_desc* desc, rva_plan* out) {
                               D.o_pad, &unpack));
       break;
     case RVA_PLAN_FUSED:
+    case RVA_PLAN_FUSED_DIRECT:
       RVA_TRY(validate_fused(D.q_pad, D.k_pad, D.v_pad, D.mask, D.B, D.N, D.H, D.d,
                              D.max_seqlen_hint, D.softmax_scale, D.dtype, D.o_pad, D.cu_seqlens,
                              D.max_seqlen, &attn));
@@ -612,6 +617,13 @@ int rva_plan_create(const rva_plan_desc* desc, rva_plan* out) {
   }
   RVA_TRY(ensure_init());
   // persistent mode owns a zeroed two-int work counter for its whole life
+  if (D.mode == RVA_PLAN_FUSED_DIRECT) {
+    RVA_TRY(ensure_init());
+    rva_plan_s* plan = new (std::nothrow) rva_plan_s{nullptr, nullptr, nullptr, true, attn, D.dtype};
+    if (!plan) return fail(RVA_ERR_INVALID, "out of host memory");
+    *out = plan;
+    return RVA_OK;
+  }
   int32_t* work = nullptr;
   if (D.mode == RVA_PLAN_PERSISTENT) {
     hipError_t e = hipMalloc(&work, 2 * sizeof(int32_t));
@@ -705,6 +717,8 @@ int rva_layers_plan_create(const rva_layers_desc* desc, rva_plan* out) {
 
 int rva_plan_launch(rva_plan plan, void* stream) {
   if (!plan) return fail(RVA_ERR_INVALID, "plan is NULL");
+  if (plan->direct)
+    return enqueue_attend(plan->attn, plan->dtype, true, static_cast<hipStream_t>(stream));
   hipError_t e = hipGraphLaunch(plan->exec, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "graph launch");
   return RVA_OK;
@@ -712,8 +726,8 @@ int rva_plan_launch(rva_plan plan, void* stream) {
 
 int rva_plan_destroy(rva_plan plan) {
   if (!plan) return RVA_OK;
-  (void)hipGraphExecDestroy(plan->exec);
-  (void)hipGraphDestroy(plan->graph);
+  if (plan->exec) (void)hipGraphExecDestroy(plan->exec);
+  if (plan->graph) (void)hipGraphDestroy(plan->graph);
   if (plan->work) (void)hipFree(plan->work);
   delete plan;
   return RVA_OK;

@@ -32,7 +32,7 @@ def _fresh_mask(seed, B, N):
     return m
 
 
-@pytest.mark.parametrize("mode", ["fused", "staged"])
+@pytest.mark.parametrize("mode", ["fused", "staged", "fused_direct"])
 def test_plan_replays_follow_mask_changes(device, mode):
     rva = _rva()
     w = W.deit_b_224(0.5)
@@ -47,6 +47,8 @@ def test_plan_replays_follow_mask_changes(device, mode):
         packed = {nm: torch.empty((B * N, H, d), dtype=q.dtype, device=device)
                   for nm in ("q", "k", "v", "o")}
         plan = rva.Plan(rva.STAGED, packed=packed, **kw)
+    elif mode == "fused_direct":
+        plan = rva.Plan(rva.FUSED_DIRECT, **kw)
     else:
         plan = rva.Plan(rva.FUSED, **kw)
     for rep in range(4):
@@ -108,4 +110,24 @@ def test_mixed_full_size_sampled(device):
         worst = max(worst, max_err(got, rows))
     _say(f"   sampled max abs err {worst:.3e}")
     assert worst <= TOL[w.dtype]
+    plan.close()
+
+
+def test_direct_plan_on_callers_stream(device):
+    """A direct-launch plan enqueues on the stream it is given (the current
+    stream by default): work queued before it on a side stream is seen."""
+    rva = _rva()
+    w = W.deit_b_224(0.8)
+    q, k, v, mask = upload(w, device)
+    ref = rva.fused(q, k, v, mask)
+    torch.cuda.synchronize()
+    out = torch.empty_like(q)
+    q2 = torch.empty_like(q)
+    plan = rva.Plan(rva.FUSED_DIRECT, q=q2, k=k, v=v, mask=mask, out=out)
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        q2.copy_(q)
+        plan.launch()
+    side.synchronize()
+    assert np.array_equal(bits(out), bits(ref))
     plan.close()
