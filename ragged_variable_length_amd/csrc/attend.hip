@@ -462,9 +462,7 @@ __device__ __forceinline__ void attend_seq16(const AttnParams& p, int n, unsigne
                                              Rsrc rq, Rsrc rk, Rsrc rv, Rsrc ro, RowOff roff,
                                              Hook last_use) {
   typedef Half16<DT> Tr;
-  typedef typename Tr::T T;
   typedef typename Tr::V8 V8;
-  typedef typename Tr::V4 V4;
   const int lane = lane_id(), w = wave_id(), g = lane >> 4, r16 = lane & 15;
   const int kc = p.kc;
   unsigned char* Ks = kvbase;
