@@ -407,3 +407,30 @@ def test_guard_bands(device):
     for nm in ("q", "k", "v"):
         tail = pbufs[nm][G + T * H * d:G + B * N * H * d].cpu().numpy()
         assert (tail == 12345).all()
+
+
+@pytest.mark.parametrize("B,N", [(10007, 7), (9001, 20)])
+def test_many_images(device, B, N):
+    """More images than one scan segment (4096) of the offsets workgroup:
+    byte-wise counting (N < 16) and 16-byte chunks straddling image
+    boundaries with a partial final chunk (N = 20, B*N not a multiple of
+    16); a grid of B*H workgroups.  Offsets and largest count bit-exact
+    through rva_pack and rva_fused; every row against the oracle."""
+    rva = _rva()
+    H = 2
+    w = W.random_workload(36 + N, B=B, N=N, H=H, dtype="f16", keep_prob=0.5,
+                          name=f"many_images_{B}x{N}")
+    _say(f"[many images] B={B} N={N} H={H}")
+    q, k, v, mask = upload(w, device)
+    cu = torch.empty(B + 1, dtype=torch.int32, device=device)
+    mx = torch.empty(1, dtype=torch.int32, device=device)
+    o = rva.fused(q, k, v, mask, cu_seqlens=cu, max_seqlen=mx)
+    pk = rva.pack(q, k, v, mask)
+    torch.cuda.synchronize()
+    ref, cu_ref, mx_ref, idx_ref = oracle.pack_attend_unpack(w.q, w.k, w.v, w.mask, w.dtype)
+    assert np.array_equal(cu.cpu().numpy(), cu_ref)
+    assert int(mx.item()) == int(mx_ref)
+    assert np.array_equal(pk["cu_seqlens"].cpu().numpy(), cu_ref)
+    assert int(pk["max_seqlen"].item()) == int(mx_ref)
+    assert max_err(f64(o), ref) <= TOL["f16"]
+    assert not bits(o)[w.mask == 0].any()
