@@ -44,7 +44,9 @@ WORKLOADS = [("deit_s", lambda: W.deit_s_224_threshold_l2()),
              ("deit_b_p0", lambda: W.deit_b_224(0.0)),
              ("deit_b_384", lambda: W.deit_b_384()),
              ("tiny_counts", lambda: W.random_workload(seed=5, B=3, N=40, H=2, dtype="bf16",
-                                                        counts=[40, 0, 1]))]
+                                                        counts=[40, 0, 1])),
+             # fp32 inputs: the persistent entry point runs the one-launch kernel
+             ("tiny_f32", lambda: W.tiny())]
 
 
 @pytest.mark.parametrize("name,make", WORKLOADS, ids=[n for n, _ in WORKLOADS])
