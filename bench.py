@@ -444,6 +444,8 @@ PROFILE_COMMANDS = {
              "-d $R/gpurun_out/prof_fetch -o fused -- python3 $R/bench.py --profile",
     "write": _ROCPROF + "timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE --output-format csv "
              "-d $R/gpurun_out/prof_write -o fused -- python3 $R/bench.py --profile",
+    "all": _ROCPROF + "rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/prof_all "
+           "-o bench -- python3 $R/bench.py --no-cpu",
     "util": _ROCPROF + "timeout -s KILL 90 rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_ACTIVE_INST_VALU "
             "SQ_BUSY_CU_CYCLES SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_VALU_TRANS_F32 SQ_WAVE_CYCLES "
             "SQ_INSTS_LDS GRBM_GUI_ACTIVE --output-format csv -d $R/gpurun_out/prof_util -o fused "
@@ -534,6 +536,38 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, cmds):
     print(json.dumps(out))
 
 
+def summarize_all(trace_dir, cmds, top=30):
+    """Every kernel of a full bench run, grouped by kernel and launch shape
+    (each grid size belongs to one workload and launch form): calls and
+    median / mean / min duration per dispatch."""
+    import glob
+    rows = _read_csv(glob.glob(os.path.join(trace_dir, "*kernel_trace.csv"))[0])
+    groups = {}
+    for r in rows:
+        wg = int(r["Workgroup_Size_X"]) * int(r["Workgroup_Size_Y"]) * int(r["Workgroup_Size_Z"])
+        grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"]) // max(wg, 1)
+        name = r["Kernel_Name"]
+        name = name[:60] + ("..." if len(name) > 60 else "")
+        groups.setdefault((name, grid, wg), []).append(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    order = sorted(groups.items(), key=lambda kv: -sum(kv[1]))[:top]
+    lines = ["# All kernels of a full bench run: durations by kernel and launch shape", "",
+             "Command (from the repository root, after building):", "",
+             "```", cmds["all"], "```", "",
+             "Grouped by kernel name, workgroups per launch and threads per workgroup; each launch shape "
+             "belongs to one workload and launch form of the bench (for example the fused kernel with "
+             "6529 workgroups is the 1024-image mixed batch: 960 images in head pairs, the last 64 one "
+             "head per workgroup, and the offsets workgroup). The largest groups by total time:", "",
+             "| kernel | workgroups | threads | calls | median us | mean us | min us |",
+             "|---|---|---|---|---|---|---|"]
+    for (name, grid, wg), d in order:
+        lines.append(f"| `{name}` | {grid} | {wg} | {len(d)} | {statistics.median(d):.2f} | "
+                     f"{statistics.mean(d):.2f} | {min(d):.2f} |")
+    with open(os.path.join(ROOT, "profiles", "bench_all_kernels_trace.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def summarize_util(util_dir, cmds):
     """Matrix-core and VALU utilisation of the fused kernel from the "util"
     counter run: MfmaUtil = MFMA busy cycles / (GUI-active cycles x SIMDs),
@@ -595,9 +629,14 @@ def main():
                     help="profiling target: a calibration copy, then the headline only")
     ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write the profiles/ summaries from rocprofv3 output of --profile runs")
+    ap.add_argument("--summarize-all", metavar="TRACE_DIR",
+                    help="write the profiles/ summary of every kernel from a traced full bench run")
     ap.add_argument("--summarize-util", metavar="UTIL_DIR",
                     help="write the profiles/ utilisation summary from the rocprofv3 counter run")
     args = ap.parse_args()
+    if args.summarize_all:
+        summarize_all(args.summarize_all, PROFILE_COMMANDS)
+        return
     if args.summarize_util:
         summarize_util(args.summarize_util, PROFILE_COMMANDS)
         return
