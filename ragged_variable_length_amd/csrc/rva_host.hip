@@ -376,8 +376,8 @@ int device_cus(int* out) {
 // How the fused 16-bit form groups heads: pairs of an image's heads per
 // workgroup only when the pairs still fill every resident slot (3 per CU)
 // at least twice over; the images dispatched last (about one slot-fill of
-// single heads) stay unpaired.  Returns the number of work items (grid
-// positions, not counting the offsets workgroup).
+// single heads) stay unpaired.  `items` (if not NULL) receives the number
+// of work items (grid positions, not counting the offsets workgroup).
 int group_heads(rva::AttnParams* p, int dtype, bool fused, long long* items) {
   p->heads_per_wg = 1;
   p->tail_b = 0;
@@ -392,7 +392,8 @@ int group_heads(rva::AttnParams* p, int dtype, bool fused, long long* items) {
     }
   }
   const int hg = p->heads_per_wg;
-  *items = (long long)(p->B - p->tail_b) * ((p->H + hg - 1) / hg) + (long long)p->tail_b * p->H;
+  if (items)
+    *items = (long long)(p->B - p->tail_b) * ((p->H + hg - 1) / hg) + (long long)p->tail_b * p->H;
   return RVA_OK;
 }
 
@@ -414,8 +415,7 @@ int enqueue_attend_persistent(const rva::AttnParams& p0, int dtype, hipStream_t 
 int enqueue_attend(const rva::AttnParams& p0, int dtype, bool fused, hipStream_t s) {
   RVA_TRY(ensure_init());
   rva::AttnParams p = p0;
-  long long items = 0;
-  RVA_TRY(group_heads(&p, dtype, fused, &items));
+  RVA_TRY(group_heads(&p, dtype, fused, nullptr));
   hipError_t e = rva::launch_attend(p, dtype, fused, s);
   if (e != hipSuccess) return hip_fail(e, fused ? "fused launch" : "attention launch");
   return RVA_OK;
@@ -616,14 +616,14 @@ int rva_plan_create(const rva_plan_desc* desc, rva_plan* out) {
       return fail(RVA_ERR_INVALID, "unknown plan mode %d", D.mode);
   }
   RVA_TRY(ensure_init());
-  // persistent mode owns a zeroed two-int work counter for its whole life
+  // direct mode: no graph, the validated launch is kept and enqueued as is
   if (D.mode == RVA_PLAN_FUSED_DIRECT) {
-    RVA_TRY(ensure_init());
     rva_plan_s* plan = new (std::nothrow) rva_plan_s{nullptr, nullptr, nullptr, true, attn, D.dtype};
     if (!plan) return fail(RVA_ERR_INVALID, "out of host memory");
     *out = plan;
     return RVA_OK;
   }
+  // persistent mode owns a zeroed two-int work counter for its whole life
   int32_t* work = nullptr;
   if (D.mode == RVA_PLAN_PERSISTENT) {
     hipError_t e = hipMalloc(&work, 2 * sizeof(int32_t));
