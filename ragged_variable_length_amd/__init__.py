@@ -142,47 +142,100 @@ def dtype_code(t: torch.Tensor) -> int:
     return _DTYPES[t.dtype]
 
 
-def _mask_u8(mask: torch.Tensor) -> torch.Tensor:
+def _dev(t, name: str, *, dtype=None, shape=None, numel=None):
+    """Check one tensor argument before its pointer reaches the library: a
+    torch tensor on the current device, contiguous, of the given dtype and
+    shape (or with at least `numel` elements).  Raises before anything is
+    enqueued; returns the tensor."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor (got {type(t).__name__})")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor (got one on {t.device})")
+    if _cur_device is not None and t.device.index != _cur_device():
+        raise ValueError(f"{name} is on {t.device}, not on the current device")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} must hold at least {numel} elements (got {t.numel()})")
+    return t
+
+
+def _opt(t, name: str, **kw):
+    return None if t is None else _dev(t, name, **kw)
+
+
+def _mask_u8(mask, B=None, N=None):
+    """The keep-mask as uint8 [B, N] (bool is viewed as uint8), checked."""
+    if not isinstance(mask, torch.Tensor):
+        raise TypeError("mask must be a torch tensor")
     if mask.dtype == torch.bool:
-        return mask.view(torch.uint8)
-    if mask.dtype != torch.uint8:
+        mask = mask.view(torch.uint8)
+    elif mask.dtype != torch.uint8:
         raise TypeError("mask must be uint8 or bool")
+    if mask.dim() != 2:
+        raise ValueError(f"mask must be [B, N] (got {tuple(mask.shape)})")
+    _dev(mask, "mask", shape=(mask.shape[0] if B is None else B, mask.shape[1] if N is None else N))
     return mask
 
 
-def _req(t: torch.Tensor, name: str):
-    if not t.is_cuda or not t.is_contiguous():
-        raise ValueError(f"{name} must be a contiguous device tensor")
+def _qkv(q, k, v):
+    """Padded q/k/v: [B, N, H, 64] of one supported dtype, identical shapes."""
+    _dev(q, "q")
+    if q.dim() != 4 or q.shape[3] != HEAD_DIM:
+        raise ValueError(f"q must be [B, N, H, {HEAD_DIM}] (got {tuple(q.shape)})")
+    dtype_code(q)
+    _dev(k, "k", dtype=q.dtype, shape=q.shape)
+    _dev(v, "v", dtype=q.dtype, shape=q.shape)
+    return tuple(q.shape)
+
+
+def _offsets(cu_seqlens, max_seqlen, B):
+    _opt(cu_seqlens, "cu_seqlens", dtype=torch.int32, shape=(B + 1,))
+    _opt(max_seqlen, "max_seqlen", dtype=torch.int32, numel=1)
 
 
 def pack(q, k, v, mask, *, outputs=None, kept_index=True, stream=None):
     """Kept counts, cu_seqlens, max_seqlen and packed q/k/v (capacity B*N rows).
 
-    q/k/v: [B,N,H,64] device tensors (any may be None); mask: [B,N] uint8/bool.
-    Returns dict with q, k, v (packed, [B*N,H,64] capacity), cu_seqlens,
-    max_seqlen ([1] int32) and kept_index ([B*N] capacity int32 or None).
+    q/k/v: [B,N,H,64] device tensors (any may be None, the given ones of one
+    shape and dtype); mask: [B,N] uint8/bool.  Returns dict with q, k, v
+    (packed, [B*N,H,64] capacity), cu_seqlens, max_seqlen ([1] int32) and
+    kept_index ([B*N] capacity int32 or None).  Caller-given outputs must
+    have those capacities.
     """
-    ref = next(t for t in (q, k, v) if t is not None) if any(t is not None for t in (q, k, v)) else None
-    if ref is None:
+    given = [(nm, t) for nm, t in (("q", q), ("k", k), ("v", v)) if t is not None]
+    if not given:
         raise ValueError("at least one of q, k, v is needed")
+    ref = _dev(given[0][1], given[0][0])
+    if ref.dim() != 4 or ref.shape[3] != HEAD_DIM:
+        raise ValueError(f"{given[0][0]} must be [B, N, H, {HEAD_DIM}] (got {tuple(ref.shape)})")
+    dtype_code(ref)
+    for nm, t in given[1:]:
+        _dev(t, nm, dtype=ref.dtype, shape=ref.shape)
     B, N, H, d = ref.shape
-    m = _mask_u8(mask)
+    m = _mask_u8(mask, B, N)
     out = dict(outputs or {})
     dev = ref.device
     for name, t in (("q", q), ("k", k), ("v", v)):
         if t is not None:
-            _req(t, name)
-            if name not in out:
+            if out.get(name) is None:
                 out[name] = torch.empty((B * N, H, d), dtype=t.dtype, device=dev)
+            _dev(out[name], f"outputs[{name!r}]", dtype=t.dtype, numel=B * N * H * d)
         else:
             out[name] = None
-    if "cu_seqlens" not in out:
+    if out.get("cu_seqlens") is None:
         out["cu_seqlens"] = torch.empty(B + 1, dtype=torch.int32, device=dev)
-    if "max_seqlen" not in out:
+    if out.get("max_seqlen") is None:
         out["max_seqlen"] = torch.empty(1, dtype=torch.int32, device=dev)
-    if kept_index and "kept_index" not in out:
+    if kept_index and out.get("kept_index") is None:
         out["kept_index"] = torch.empty(B * N, dtype=torch.int32, device=dev)
     out.setdefault("kept_index", None)
+    _offsets(out["cu_seqlens"], out["max_seqlen"], B)
+    _opt(out["kept_index"], "kept_index", dtype=torch.int32, numel=B * N)
     _check(lib().rva_pack(_ptr(q), _ptr(k), _ptr(v), _ptr(m), B, N, H, d, dtype_code(ref),
                           _ptr(out["q"]), _ptr(out["k"]), _ptr(out["v"]), _ptr(out["cu_seqlens"]),
                           _ptr(out["max_seqlen"]), _ptr(out["kept_index"]), _stream(stream)),
@@ -198,24 +251,48 @@ def index(mask, *, out=None, stream=None):
     B, N = m.shape
     out = dict(out or {})
     dev = m.device
-    out.setdefault("cu_seqlens", torch.empty(B + 1, dtype=torch.int32, device=dev))
-    out.setdefault("max_seqlen", torch.empty(1, dtype=torch.int32, device=dev))
-    out.setdefault("kept_index", torch.empty(B * N, dtype=torch.int32, device=dev))
+    if out.get("cu_seqlens") is None:
+        out["cu_seqlens"] = torch.empty(B + 1, dtype=torch.int32, device=dev)
+    if out.get("max_seqlen") is None:
+        out["max_seqlen"] = torch.empty(1, dtype=torch.int32, device=dev)
+    if out.get("kept_index") is None:
+        out["kept_index"] = torch.empty(B * N, dtype=torch.int32, device=dev)
+    _offsets(out["cu_seqlens"], out["max_seqlen"], B)
+    _dev(out["kept_index"], "kept_index", dtype=torch.int32, numel=B * N)
     _check(lib().rva_pack(None, None, None, _ptr(m), B, N, 1, HEAD_DIM, F16, None, None, None,
                           _ptr(out["cu_seqlens"]), _ptr(out["max_seqlen"]),
                           _ptr(out["kept_index"]), _stream(stream)), "rva_pack")
     return out
 
 
+def _packed(t, name, ref=None):
+    """Packed rows [rows, H, 64] (matching `ref` in shape and dtype)."""
+    if ref is not None:
+        return _dev(t, name, dtype=ref.dtype, shape=ref.shape)
+    _dev(t, name)
+    if t.dim() != 3 or t.shape[2] != HEAD_DIM:
+        raise ValueError(f"{name} must be [rows, H, {HEAD_DIM}] (got {tuple(t.shape)})")
+    dtype_code(t)
+    return t
+
+
 def ragged_attend(q, k, v, cu_seqlens, max_seqlen: int, *, scale: float | None = None, out=None,
                   stream=None):
-    """Attention over packed [T,H,64] q/k/v with offsets cu_seqlens [B+1]."""
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        _req(t, name)
+    """Attention over packed [T,H,64] q/k/v with offsets cu_seqlens [B+1].
+
+    cu_seqlens is int32 on the device; its last entry (T) must not exceed the
+    rows of q/k/v/out (the values are device data and are not read here)."""
+    _packed(q, "q")
+    _packed(k, "k", q)
+    _packed(v, "v", q)
+    _dev(cu_seqlens, "cu_seqlens", dtype=torch.int32)
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens must be int32 [B+1] with B >= 1")
     H, d = q.shape[1], q.shape[2]
     B = cu_seqlens.shape[0] - 1
     if out is None:
         out = torch.empty_like(q)
+    _packed(out, "out", q)
     _check(lib().rva_ragged_attend(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), B, H, d,
                                    int(max_seqlen), float(scale or 0.0), dtype_code(q), _ptr(out),
                                    _stream(stream)), "rva_ragged_attend")
@@ -226,23 +303,31 @@ def unpack(o_packed, cu_seqlens, mask, *, out=None, stream=None):
     """Packed [T,H,64] rows -> padded [B,N,H,64]; pruned rows are +0."""
     m = _mask_u8(mask)
     B, N = m.shape
+    _packed(o_packed, "o_packed")
+    _dev(cu_seqlens, "cu_seqlens", dtype=torch.int32, shape=(B + 1,))
     H, d = o_packed.shape[1], o_packed.shape[2]
     if out is None:
         out = torch.empty((B, N, H, d), dtype=o_packed.dtype, device=o_packed.device)
+    _dev(out, "out", dtype=o_packed.dtype, shape=(B, N, H, d))
     _check(lib().rva_unpack(_ptr(o_packed), _ptr(cu_seqlens), _ptr(m), B, N, H, d,
                             dtype_code(o_packed), _ptr(out), _stream(stream)), "rva_unpack")
     return out
 
 
+def _fused_args(q, k, v, mask, out, cu_seqlens, max_seqlen):
+    B, N, H, d = _qkv(q, k, v)
+    m = _mask_u8(mask, B, N)
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out", dtype=q.dtype, shape=q.shape)
+    _offsets(cu_seqlens, max_seqlen, B)
+    return m, out, (B, N, H, d)
+
+
 def fused(q, k, v, mask, *, max_seqlen_hint: int = 0, scale: float | None = None, out=None,
           cu_seqlens=None, max_seqlen=None, stream=None):
     """Whole path in one launch: padded [B,N,H,64] in, padded out."""
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        _req(t, name)
-    m = _mask_u8(mask)
-    B, N, H, d = q.shape
-    if out is None:
-        out = torch.empty_like(q)
+    m, out, (B, N, H, d) = _fused_args(q, k, v, mask, out, cu_seqlens, max_seqlen)
     _check(lib().rva_fused(_ptr(q), _ptr(k), _ptr(v), _ptr(m), B, N, H, d, int(max_seqlen_hint),
                            float(scale or 0.0), dtype_code(q), _ptr(out), _ptr(cu_seqlens),
                            _ptr(max_seqlen), _stream(stream)), "rva_fused")
@@ -252,13 +337,11 @@ def fused(q, k, v, mask, *, max_seqlen_hint: int = 0, scale: float | None = None
 def fused_persistent(q, k, v, mask, work, *, max_seqlen_hint: int = 0, scale: float | None = None,
                      out=None, cu_seqlens=None, max_seqlen=None, stream=None):
     """fused() as a persistent grid.  work: int32 [2] device tensor, zero
-    before the first call (every call leaves it zero again)."""
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        _req(t, name)
-    m = _mask_u8(mask)
-    B, N, H, d = q.shape
-    if out is None:
-        out = torch.empty_like(q)
+    before the first call (every call leaves it zero again).  Only one call
+    may be in flight on one work buffer: calls on different streams that may
+    overlap need distinct buffers."""
+    m, out, (B, N, H, d) = _fused_args(q, k, v, mask, out, cu_seqlens, max_seqlen)
+    _dev(work, "work", dtype=torch.int32, numel=2)
     _check(lib().rva_fused_persistent(_ptr(q), _ptr(k), _ptr(v), _ptr(m), B, N, H, d,
                                       int(max_seqlen_hint), float(scale or 0.0), dtype_code(q),
                                       _ptr(out), _ptr(cu_seqlens), _ptr(max_seqlen), _ptr(work),
@@ -270,13 +353,22 @@ def threshold_l2_mask(x, keep_quantile: float, *, out=None, stream=None):
     """Threshold-l2 keep-mask of embeddings x [B,N,C]: uint8 [B,N], CLS kept,
     patch kept when its L2 norm reaches the per-image keep_quantile of the
     patch norms."""
-    _req(x, "x")
+    _dev(x, "x")
+    if x.dim() != 3:
+        raise ValueError(f"x must be [B, N, C] (got {tuple(x.shape)})")
+    dtype_code(x)
     B, N, C = x.shape
     if out is None:
         out = torch.empty((B, N), dtype=torch.uint8, device=x.device)
+    _dev(out, "out", dtype=torch.uint8, shape=(B, N))
     _check(lib().rva_threshold_l2_mask(_ptr(x), B, N, C, dtype_code(x), float(keep_quantile),
                                        _ptr(out), _stream(stream)), "rva_threshold_l2_mask")
     return out
+
+
+def _weight(w, b, rows, C, dtype, wname, bname):
+    _dev(w, wname, dtype=dtype, shape=(rows, C))
+    _opt(b, bname, dtype=dtype, shape=(rows,))
 
 
 def qkv_projection(x, cu_seqlens, w_qkv, b_qkv=None, *, kept_index=None, B=None, N=None,
@@ -287,15 +379,25 @@ def qkv_projection(x, cu_seqlens, w_qkv, b_qkv=None, *, kept_index=None, B=None,
     without (then B and N give the capacity B*N).  Returns packed q, k, v of
     capacity B*N rows, [B*N, C] each (rows past T = cu_seqlens[B] untouched).
     """
-    _req(x, "x")
+    _dev(x, "x")
+    dtype_code(x)
     C = x.shape[-1]
     if kept_index is not None:
+        if x.dim() != 3:
+            raise ValueError(f"x must be padded [B, N, C] with kept_index (got {tuple(x.shape)})")
         B, N = x.shape[0], x.shape[1]
+        _dev(kept_index, "kept_index", dtype=torch.int32, numel=B * N)
     if B is None or N is None:
         raise ValueError("packed input needs B and N")
+    if kept_index is None:
+        _dev(x, "x", numel=B * N * C)
+    _dev(cu_seqlens, "cu_seqlens", dtype=torch.int32, shape=(B + 1,))
+    _weight(w_qkv, b_qkv, 3 * C, C, x.dtype, "w_qkv", "b_qkv")
     if out is None:
         out = tuple(torch.empty((B * N, C), dtype=x.dtype, device=x.device) for _ in range(3))
     q, k, v = out
+    for nm, t in (("q", q), ("k", k), ("v", v)):
+        _dev(t, f"out {nm}", dtype=x.dtype, numel=B * N * C)
     _check(lib().rva_qkv_projection(_ptr(x), _ptr(kept_index), _ptr(cu_seqlens), B, N, C,
                                     _ptr(w_qkv), _ptr(b_qkv), dtype_code(x), _ptr(q), _ptr(k),
                                     _ptr(v), _stream(stream)), "rva_qkv_projection")
@@ -309,17 +411,30 @@ def out_projection(o, cu_seqlens, w_o, b_o=None, *, kept_index=None, mask=None, 
     With kept_index and mask: y is padded [B,N,C], pruned rows +0, residual
     padded.  Without: y packed [B*N, C] (capacity), residual packed.
     """
-    _req(o, "o")
+    _dev(o, "o")
+    dtype_code(o)
     C = o.shape[-1]
     m = None
     if kept_index is not None:
+        if mask is None:
+            raise ValueError("mask is needed with kept_index")
         m = _mask_u8(mask)
         B, N = m.shape
+        _dev(kept_index, "kept_index", dtype=torch.int32, numel=B * N)
     if B is None or N is None:
         raise ValueError("B and N are needed")
+    _dev(o, "o", numel=B * N * C)
+    _dev(cu_seqlens, "cu_seqlens", dtype=torch.int32, shape=(B + 1,))
+    _weight(w_o, b_o, C, C, o.dtype, "w_o", "b_o")
+    shape = (B, N, C) if kept_index is not None else None
     if out is None:
-        shape = (B, N, C) if kept_index is not None else (B * N, C)
-        out = torch.empty(shape, dtype=o.dtype, device=o.device)
+        out = torch.empty(shape or (B * N, C), dtype=o.dtype, device=o.device)
+    if shape:
+        _dev(out, "out", dtype=o.dtype, shape=shape)
+        _opt(residual, "residual", dtype=o.dtype, shape=shape)
+    else:
+        _dev(out, "out", dtype=o.dtype, numel=B * N * C)
+        _opt(residual, "residual", dtype=o.dtype, numel=B * N * C)
     _check(lib().rva_out_projection(_ptr(o), _ptr(kept_index), _ptr(cu_seqlens), _ptr(m), B, N, C,
                                     _ptr(w_o), _ptr(b_o), _ptr(residual), dtype_code(o), _ptr(out),
                                     _stream(stream)), "rva_out_projection")
@@ -336,8 +451,10 @@ class Plan:
     (mode FUSED_DIRECT) the fused launch validated once and enqueued directly
     by every launch().
 
-    Tensors given here are kept alive by the plan; their contents may change
-    between launches, their addresses may not.
+    Tensors given here are checked as the direct calls check them and kept
+    alive by the plan; their contents may change between launches, their
+    addresses may not.  A PERSISTENT plan owns one work counter: one launch
+    of it may be in flight at a time.
     """
 
     def __init__(self, mode: int, *, q=None, k=None, v=None, mask=None, out=None, scale=None,
@@ -350,24 +467,33 @@ class Plan:
         desc.mode = mode
         desc.d = HEAD_DIM
         if mode != EMPTY:
-            B, N, H, d = q.shape
+            m, out, (B, N, H, d) = _fused_args(q, k, v, mask, out, cu_seqlens, max_seqlen)
+            self._keep.append(out)
             desc.B, desc.N, desc.H, desc.d = B, N, H, d
             desc.dtype = dtype_code(q)
             desc.max_seqlen_hint = int(max_seqlen_hint)
             desc.softmax_scale = float(scale or 0.0)
             desc.q_pad, desc.k_pad, desc.v_pad = q.data_ptr(), k.data_ptr(), v.data_ptr()
-            desc.mask = _mask_u8(mask).data_ptr()
+            desc.mask = m.data_ptr()
             desc.o_pad = out.data_ptr()
+            if mode == STAGED:
+                if packed is None or cu_seqlens is None:
+                    raise ValueError("a staged plan needs packed buffers and cu_seqlens")
+                for nm in ("q", "k", "v", "o"):
+                    _dev(packed[nm], f"packed[{nm!r}]", dtype=q.dtype, numel=B * N * H * d)
             if packed is not None:
                 desc.q_packed = packed["q"].data_ptr()
                 desc.k_packed = packed["k"].data_ptr()
                 desc.v_packed = packed["v"].data_ptr()
                 desc.o_packed = packed["o"].data_ptr()
+            _opt(kept_index, "kept_index", dtype=torch.int32, numel=B * N)
             desc.cu_seqlens = cu_seqlens.data_ptr() if cu_seqlens is not None else None
             desc.max_seqlen = max_seqlen.data_ptr() if max_seqlen is not None else None
             desc.kept_index = kept_index.data_ptr() if kept_index is not None else None
             if mode == L2_FUSED:
-                _req(x, "x")
+                _dev(x, "x")
+                if x.dim() != 3 or tuple(x.shape[:2]) != (B, N):
+                    raise ValueError(f"x must be [{B}, {N}, C] (got {tuple(x.shape)})")
                 desc.x = x.data_ptr()
                 desc.C = x.shape[2]
                 desc.x_dtype = dtype_code(x)
@@ -404,11 +530,17 @@ class LayersPlan(Plan):
     """
 
     def __init__(self, x, mask, weights, *, out=None, scale=None, max_seqlen_hint: int = 0):
-        _req(x, "x")
+        _dev(x, "x")
+        if x.dim() != 3 or x.shape[2] % HEAD_DIM:
+            raise ValueError(f"x must be [B, N, C] with C a multiple of {HEAD_DIM}")
+        dtype_code(x)
         B, N, C = x.shape
         H = C // HEAD_DIM
         L = len(weights)
-        m = _mask_u8(mask)
+        m = _mask_u8(mask, B, N)
+        for l, wd in enumerate(weights):
+            _weight(wd["w_qkv"], wd.get("b_qkv"), 3 * C, C, x.dtype, f"w_qkv[{l}]", f"b_qkv[{l}]")
+            _weight(wd["w_o"], wd.get("b_o"), C, C, x.dtype, f"w_o[{l}]", f"b_o[{l}]")
         dev = x.device
         self.scratch = {nm: torch.empty((B * N, C), dtype=x.dtype, device=dev)
                         for nm in ("resid", "q", "k", "v", "o")}
@@ -416,6 +548,7 @@ class LayersPlan(Plan):
         self.max_seqlen = torch.empty(1, dtype=torch.int32, device=dev)
         self.kept_index = torch.empty(B * N, dtype=torch.int32, device=dev)
         self.out = out if out is not None else torch.empty_like(x)
+        _dev(self.out, "out", dtype=x.dtype, shape=x.shape)
         self._keep = [x, m, weights, self.scratch, self.out]
         arr = lambda key: (ctypes.c_void_p * L)(*[
             (wd[key].data_ptr() if wd.get(key) is not None else None) for wd in weights])

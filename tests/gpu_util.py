@@ -76,3 +76,39 @@ def check_linear(got, ref, mag_bound, dtype, what):
     assert np.isfinite(got).all(), what
     bad = err > tol
     assert not bad.any(), (what, float(err.max()), np.argwhere(bad)[:4])
+
+
+# The 1024-image mixed batch and its oracle output, computed once per test
+# session and shared by every full-size check (about 10 s of CPU work).
+_MIXED = {}
+
+
+def mixed_full():
+    """dict(w=workload, ref=oracle O at the kept positions [T, H, 64] float64
+    in kept-index order, cu=cu_seqlens, mx=max_seqlen, keep=bool [B, N])."""
+    if not _MIXED:
+        import oracle
+        import workloads as W
+        w = W.mixed_peak()
+        ref, cu, mx, _ = oracle.pack_attend_unpack(w.q, w.k, w.v, w.mask, w.dtype)
+        keep = w.mask.astype(bool)
+        _MIXED.update(w=w, ref=ref[keep], cu=cu, mx=mx, keep=keep)
+        del ref
+    return _MIXED
+
+
+def check_mixed_full(out: torch.Tensor, what: str, cu=None, mx=None) -> float:
+    """Every element of a padded device output of the mixed batch against the
+    oracle: pruned rows exactly +0, kept rows within the fp16 bound; offsets
+    bit-exact when given.  Returns the max abs error."""
+    m = mixed_full()
+    b = bits(out)
+    assert (b[~m["keep"]] == 0).all(), f"{what}: pruned rows not +0"
+    got = b[m["keep"]].view(np.float16).astype(np.float64)
+    err = max_err(got, m["ref"])
+    assert err <= TOL["f16"], f"{what}: max abs err {err:.3e}"
+    if cu is not None:
+        assert np.array_equal(cu.cpu().numpy(), m["cu"]), f"{what}: cu_seqlens"
+    if mx is not None:
+        assert int(mx.item()) == int(m["mx"]), f"{what}: max_seqlen"
+    return err

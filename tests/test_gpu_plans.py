@@ -78,39 +78,69 @@ def test_empty_plan_and_empty_launches(device):
     p.close()
 
 
-def test_mixed_full_size_sampled(device):
-    """The 1024-image mixed batch through the captured fused launch (the bench's
-    configuration): offsets exactly, attention on sampled (image, head) pairs,
-    pruned rows zero everywhere."""
-    rva = _rva()
-    w = W.mixed_peak()
-    _say(f"[mixed] B={w.B} T={w.total_kept}")
+def _mixed_dev(device):
+    from gpu_util import mixed_full
+    w = mixed_full()["w"]
     q, k, v, mask = upload(w, device)
-    B, N, H, d = q.shape
-    out = torch.empty_like(q)
-    cu = torch.empty(B + 1, dtype=torch.int32, device=device)
-    mx = torch.empty(1, dtype=torch.int32, device=device)
-    plan = rva.Plan(rva.FUSED, q=q, k=k, v=v, mask=mask, out=out, cu_seqlens=cu, max_seqlen=mx)
-    plan.launch()
-    plan.launch()
+    B = w.B
+    return w, q, k, v, mask, (torch.empty_like(q), torch.empty(B + 1, dtype=torch.int32, device=device),
+                              torch.empty(1, dtype=torch.int32, device=device))
+
+
+@pytest.mark.parametrize("form", ["fused_graph", "fused_direct_plan", "fused_call"])
+def test_mixed_full_size_fused(device, form):
+    """The 1024-image mixed batch (12,288 image-head pairs) through the fused
+    single launch, as the bench times it (direct call, direct-launch plan)
+    and as a captured graph: offsets exactly, every kept element against the
+    oracle, pruned rows +0."""
+    from gpu_util import check_mixed_full
+    rva = _rva()
+    w, q, k, v, mask, (out, cu, mx) = _mixed_dev(device)
+    _say(f"[mixed] {form} B={w.B} T={w.total_kept}")
+    hint = int(w.counts.max())
+    if form == "fused_call":
+        for _ in range(2):
+            rva.fused(q, k, v, mask, out=out, cu_seqlens=cu, max_seqlen=mx, max_seqlen_hint=hint)
+    else:
+        mode = rva.FUSED if form == "fused_graph" else rva.FUSED_DIRECT
+        plan = rva.Plan(mode, q=q, k=k, v=v, mask=mask, out=out, cu_seqlens=cu, max_seqlen=mx,
+                        max_seqlen_hint=hint)
+        plan.launch()
+        plan.launch()
+        plan.close()
     torch.cuda.synchronize()
-    cu_ref, mx_ref = oracle.seqlens(w.mask)
-    assert cu.cpu().numpy().tolist() == cu_ref.tolist()
-    assert int(mx.item()) == mx_ref
-    ob = out.cpu()
-    assert (bits(ob)[w.mask == 0] == 0).all()
-    rng = np.random.Generator(np.random.PCG64(5))
-    counts = w.counts
-    picks = [(int(np.argmax(counts)), 0), (int(np.argmin(counts)), H - 1)]
-    picks += [(int(b), int(h)) for b, h in zip(rng.integers(0, B, 30), rng.integers(0, H, 30))]
-    worst = 0.0
-    for b, h in picks:
-        keep, rows = oracle.attend_image_head(w.q, w.k, w.v, w.mask, w.dtype, b, h)
-        got = ob[b, keep, h].float().numpy().astype(np.float64)
-        worst = max(worst, max_err(got, rows))
-    _say(f"   sampled max abs err {worst:.3e}")
-    assert worst <= TOL[w.dtype]
-    plan.close()
+    err = check_mixed_full(out, form, cu, mx)
+    _say(f"   max abs err over every element {err:.3e}")
+
+
+@pytest.mark.parametrize("form", ["calls", "staged_graph"])
+def test_mixed_full_size_staged(device, form):
+    """The mixed batch through the separate pack -> ragged attention ->
+    unpack launches (direct calls, and the staged graph): packed offsets and
+    kept index exactly, every element of the padded output against the
+    oracle."""
+    from gpu_util import check_mixed_full
+    rva = _rva()
+    w, q, k, v, mask, (out, cu, mx) = _mixed_dev(device)
+    B, N, H, d = q.shape
+    _say(f"[mixed] staged {form}")
+    if form == "calls":
+        pk = rva.pack(q, k, v, mask)
+        o = torch.empty_like(pk["q"])
+        rva.ragged_attend(pk["q"], pk["k"], pk["v"], pk["cu_seqlens"], int(w.counts.max()), out=o)
+        rva.unpack(o, pk["cu_seqlens"], mask, out=out)
+        torch.cuda.synchronize()
+        T = w.total_kept
+        assert np.array_equal(pk["kept_index"][:T].cpu().numpy(), oracle.kept_index(w.mask))
+        check_mixed_full(out, form, pk["cu_seqlens"], pk["max_seqlen"])
+    else:
+        packed = {nm: torch.empty((B * N, H, d), dtype=q.dtype, device=device) for nm in "qkvo"}
+        plan = rva.Plan(rva.STAGED, q=q, k=k, v=v, mask=mask, out=out, packed=packed,
+                        cu_seqlens=cu, max_seqlen=mx, max_seqlen_hint=N)
+        plan.launch()
+        torch.cuda.synchronize()
+        check_mixed_full(out, form, cu, mx)
+        plan.close()
 
 
 def test_direct_plan_on_callers_stream(device):

@@ -158,8 +158,8 @@ def test_out_packed_inplace_residual(device):
 def test_block_stagewise_full_size(device):
     """The attention block on the mixed 1024-image batch at DeiT-B width:
     offsets + kept index, QKV gather-product, ragged attention, output
-    product with scatter.  Each stage is checked on sampled rows against the
-    oracle applied to that stage's device inputs."""
+    product with scatter.  Each stage is checked on every row of every image
+    against the oracle applied to that stage's device inputs."""
     rva = _rva()
     w = W.mixed_peak()
     B, N, H = w.B, w.N, w.H
@@ -183,10 +183,9 @@ def test_block_stagewise_full_size(device):
     cu_h = cu.cpu().numpy()
     T = int(cu_h[-1])
     assert T == w.total_kept
-    rng = np.random.Generator(np.random.PCG64(3))
-    imgs = np.sort(rng.choice(B, 12, replace=False))
+    imgs = np.arange(B)
     qh, kh, vh, oh = (a.cpu().numpy()[:T] for a in (q, k, v, o))
-    # stage 1: QKV rows of the sampled images
+    # stage 1: QKV rows of every image
     rows = np.concatenate([np.arange(cu_h[b], cu_h[b + 1]) for b in imgs])
     kept = oracle.kept_index(w.mask)
     xs = oracle.decode(x.reshape(B * N, C)[kept[rows]], "f16")
@@ -196,13 +195,13 @@ def test_block_stagewise_full_size(device):
         got = part[rows].astype(np.float64)
         _check(got, ref, _bound(xs, wf[t * C:(t + 1) * C], bf[t * C:(t + 1) * C], None, "f16"),
                "f16", f"qkv {t}")
-    # stage 2: attention of the sampled images on the device's own q/k/v
+    # stage 2: attention of every image on the device's own q/k/v
     for b in imgs:
         lo, hi = int(cu_h[b]), int(cu_h[b + 1])
         sl = lambda a: oracle.decode(a[lo:hi].reshape(hi - lo, H, 64), "f16")
         ref = oracle.attend(sl(qh), sl(kh), sl(vh), np.array([0, hi - lo]))
         assert max_err(oh[lo:hi].reshape(hi - lo, H, 64).astype(np.float64), ref) <= TOL["f16"]
-    # stage 3: output rows of the sampled images on the device's own o
+    # stage 3: output rows of every image on the device's own o
     os_ = oracle.decode(oh[rows], "f16")
     wo, bo = oracle.decode(wts["w_o"], "f16"), oracle.decode(wts["b_o"], "f16")
     ref = oracle.linear(os_, wo, bo)
