@@ -135,13 +135,41 @@ int rva_fused(const void* q_pad, const void* k_pad, const void* v_pad, const uin
  * rva_fused), plus:
  *   work : int32[2] device scratch, all zero before the first call.  Every
  *          call leaves it zero again when it completes, so one buffer serves
- *          any number of stream-ordered calls; calls that may run at the same
- *          time need distinct buffers.
+ *          any number of stream-ordered calls.  Only one call may be in
+ *          flight on a buffer: two overlapping calls (different streams)
+ *          share item indices and the reset, so each computes part of the
+ *          items and output rows stay unwritten, silently.  Calls that may
+ *          run at the same time need distinct buffers.
+ * Limits: as rva_fused, and B * H < 2^30, so that the 32-bit work counter
+ * (which reaches the item count plus the resident workgroups) cannot wrap
+ * (RVA_ERR_INVALID otherwise, checked before anything is enqueued).
  */
 int rva_fused_persistent(const void* q_pad, const void* k_pad, const void* v_pad,
                          const uint8_t* mask, int B, int N, int H, int d, int max_seqlen_hint,
                          float softmax_scale, int dtype, void* o_pad, int32_t* cu_seqlens,
                          int32_t* max_seqlen, int32_t* work, void* stream);
+
+/*
+ * rva_fused_persistent_noalloc -- rva_fused_persistent for callers that
+ * cannot allocate device memory (code under HIP graph capture, serving loops
+ * and harnesses that forbid hipMalloc): the same arguments without `work`,
+ * and the same results bit for bit.  The work counter pair lives in a
+ * 256-byte array of static device memory inside the library (one copy per
+ * GPU, held until the process ends), of which a call uses 8 bytes whatever
+ * B, N and H are.  Nothing is allocated: no hipMalloc, hipFree or
+ * allocating library call.  The first call on a GPU also enqueues a
+ * one-workgroup fill kernel that zeroes the counter; every completed call
+ * leaves it zero for the next.  All calls on one GPU share that counter, so
+ * calls that may overlap on one GPU (different streams, or graphs replayed
+ * concurrently) race and leave output rows unwritten: order them on one
+ * stream.  Limits: as rva_fused_persistent (B * H < 2^30, RVA_ERR_INVALID
+ * otherwise, checked before anything is enqueued, the first call's fill
+ * kernel included).
+ */
+int rva_fused_persistent_noalloc(const void* q_pad, const void* k_pad, const void* v_pad,
+                                 const uint8_t* mask, int B, int N, int H, int d,
+                                 int max_seqlen_hint, float softmax_scale, int dtype, void* o_pad,
+                                 int32_t* cu_seqlens, int32_t* max_seqlen, void* stream);
 
 /*
  * rva_threshold_l2_mask -- the Threshold-l2 keep-mask that feeds the path
@@ -222,7 +250,9 @@ int rva_out_projection(const void* o, const int32_t* kept_index, const int32_t* 
  *                        ignored.
  *      RVA_PLAN_PERSISTENT : rva_fused_persistent (1 kernel); the plan owns
  *                        its work counter (8 bytes of device memory,
- *                        allocated and zeroed at creation, freed at destroy).
+ *                        allocated and zeroed at creation, freed at destroy),
+ *                        so one launch of the plan may be in flight at a
+ *                        time (launches on one stream).
  *      RVA_PLAN_FUSED_DIRECT : rva_fused (1 kernel) without a graph: the
  *                        arguments are validated once at creation and each
  *                        rva_plan_launch enqueues the kernel directly, which

@@ -17,6 +17,7 @@ import torch
 
 __all__ = ["RVAError", "lib", "pack", "ragged_attend", "unpack", "fused", "threshold_l2_mask",
            "qkv_projection", "out_projection", "index", "LayersPlan", "fused_persistent",
+           "fused_persistent_noalloc",
            "PERSISTENT",
            "Plan", "empty", "dtype_code", "F32", "F16", "BF16", "STAGED", "FUSED", "EMPTY",
            "L2_FUSED", "MAX_TOKENS"]
@@ -83,6 +84,7 @@ def lib() -> ctypes.CDLL:
     L.rva_unpack.argtypes = [P, P, P, I, I, I, I, I, P, P]
     L.rva_fused.argtypes = [P, P, P, P, I, I, I, I, I, F, I, P, P, P, P]
     L.rva_fused_persistent.argtypes = [P, P, P, P, I, I, I, I, I, F, I, P, P, P, P, P]
+    L.rva_fused_persistent_noalloc.argtypes = [P, P, P, P, I, I, I, I, I, F, I, P, P, P, P]
     L.rva_plan_create.argtypes = [ctypes.POINTER(_PlanDesc), ctypes.POINTER(ctypes.c_void_p)]
     L.rva_plan_launch.argtypes = [P, P]
     L.rva_layers_plan_create.argtypes = [ctypes.POINTER(_LayersDesc), ctypes.POINTER(ctypes.c_void_p)]
@@ -99,7 +101,8 @@ def lib() -> ctypes.CDLL:
     for name in ("rva_pack", "rva_ragged_attend", "rva_unpack", "rva_fused", "rva_plan_create",
                  "rva_plan_launch", "rva_plan_destroy", "rva_empty", "rva_version",
                  "rva_threshold_l2_mask", "rva_qkv_projection", "rva_out_projection",
-                 "rva_layers_plan_create", "rva_fused_persistent"):
+                 "rva_layers_plan_create", "rva_fused_persistent",
+                 "rva_fused_persistent_noalloc"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -346,6 +349,21 @@ def fused_persistent(q, k, v, mask, work, *, max_seqlen_hint: int = 0, scale: fl
                                       int(max_seqlen_hint), float(scale or 0.0), dtype_code(q),
                                       _ptr(out), _ptr(cu_seqlens), _ptr(max_seqlen), _ptr(work),
                                       _stream(stream)), "rva_fused_persistent")
+    return out
+
+
+def fused_persistent_noalloc(q, k, v, mask, *, max_seqlen_hint: int = 0,
+                             scale: float | None = None, out=None, cu_seqlens=None,
+                             max_seqlen=None, stream=None):
+    """fused_persistent() with the library's own static work counter (no
+    work buffer, nothing allocated by the library).  All calls on one GPU
+    share that counter: calls must not overlap (order them on one stream)."""
+    m, out, (B, N, H, d) = _fused_args(q, k, v, mask, out, cu_seqlens, max_seqlen)
+    _check(lib().rva_fused_persistent_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(m), B, N, H, d,
+                                              int(max_seqlen_hint), float(scale or 0.0),
+                                              dtype_code(q), _ptr(out), _ptr(cu_seqlens),
+                                              _ptr(max_seqlen), _stream(stream)),
+           "rva_fused_persistent_noalloc")
     return out
 
 

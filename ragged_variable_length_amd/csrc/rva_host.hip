@@ -1,6 +1,9 @@
 // Host side of the C ABI declared in include/rva.h: argument validation,
 // launch geometry, thread-local error text and captured launch plans.
-// Nothing here allocates device memory or synchronises with the device.
+// The call paths only enqueue work: they neither allocate device memory nor
+// synchronise with the device.  Plan creation is the exception: a persistent
+// plan allocates its 8-byte work counter (hipMalloc) and zeroes it with a
+// blocking hipMemset, and graph instantiation allocates in the runtime.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdarg.h>
@@ -397,6 +400,18 @@ int group_heads(rva::AttnParams* p, int dtype, bool fused, long long* items) {
   return RVA_OK;
 }
 
+// The persistent form's item counter is an int32 that reaches items + grid
+// (every workgroup draws one index past the last item before it leaves);
+// items and grid are each at most B*H, so B*H < 2^30 keeps it in range.
+// Pure host arithmetic: it runs before anything touches the device.
+int check_persistent_items(int B, int H) {
+  if ((long long)B * H >= (1ll << 30))
+    return fail(RVA_ERR_INVALID,
+                "persistent form: B*H = %lld work items exceed its 32-bit counter (limit 2^30)",
+                (long long)B * H);
+  return RVA_OK;
+}
+
 int enqueue_attend_persistent(const rva::AttnParams& p0, int dtype, hipStream_t s) {
   RVA_TRY(ensure_init());
   rva::AttnParams p = p0;
@@ -407,6 +422,9 @@ int enqueue_attend_persistent(const rva::AttnParams& p0, int dtype, hipStream_t 
   long long grid = (long long)rva::attend_persistent_per_cu(p.N, p.kc) * cus;
   if (grid > items) grid = items;
   if (grid < 1) grid = 1;
+  if (items + grid >= (1ll << 31))  // excluded by check_persistent_items
+    return fail(RVA_ERR_INVALID, "persistent form: %lld work items exceed its 32-bit counter",
+                items);
   hipError_t e = rva::launch_attend_persistent(p, dtype, (int)grid, s);
   if (e != hipSuccess) return hip_fail(e, "persistent launch");
   return RVA_OK;
@@ -418,6 +436,62 @@ int enqueue_attend(const rva::AttnParams& p0, int dtype, bool fused, hipStream_t
   RVA_TRY(group_heads(&p, dtype, fused, nullptr));
   hipError_t e = rva::launch_attend(p, dtype, fused, s);
   if (e != hipSuccess) return hip_fail(e, fused ? "fused launch" : "attention launch");
+  return RVA_OK;
+}
+
+}  // namespace
+
+// ---- device scratch of the allocation-free persistent entry point
+
+// The persistent form's work counter pair [next item, workgroups done] for
+// callers that cannot allocate device memory.  Every GPU the library runs on
+// holds its own copy of this array (256 bytes) until the process ends.  In
+// host code `scratch` names a host-side stand-in, not device memory: only
+// the address hipGetSymbolAddress returns for the current device may reach
+// a kernel, a copy or a fill.
+constexpr int kScratchInts = 64;
+constexpr int kScratchCounterInts = 2;  // what one call uses: one counter pair
+static_assert(kScratchCounterInts <= kScratchInts, "counter pair fits the scratch array");
+static __device__ __align__(256) int32_t scratch[kScratchInts];
+
+__global__ void zero_i32_kernel(int32_t* p, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0;
+}
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+int32_t* g_scratch_dev[kMaxDevices] = {};  // device address of `scratch`, per device
+bool g_scratch_cleared[kMaxDevices] = {};
+
+// The current device's address of `scratch`, looked up once per device with
+// that device current.  The first call on a device also enqueues, on `s`, a
+// fill kernel that zeroes the counter pair (a kernel rather than a memset,
+// so that a caller may capture it in a graph); every completed persistent
+// launch leaves the pair zero again for the next stream-ordered call.
+int scratch_counter(hipStream_t s, int32_t** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(RVA_ERR_UNSUPPORTED, "device ordinal %d beyond %d", dev, kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "scratch symbol address");
+    if (!p) return fail(RVA_ERR_HIP, "scratch symbol address is NULL");
+    g_scratch_dev[dev] = static_cast<int32_t*>(p);
+  }
+  if (!g_scratch_cleared[dev]) {
+    hipLaunchKernelGGL(zero_i32_kernel, dim3(1), dim3(64), 0, s, g_scratch_dev[dev],
+                       kScratchCounterInts);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "scratch clear launch");
+    g_scratch_cleared[dev] = true;
+  }
+  *out = g_scratch_dev[dev];
   return RVA_OK;
 }
 
@@ -557,10 +631,27 @@ int rva_fused_persistent(const void* q_pad, const void* k_pad, const void* v_pad
   RVA_TRY(validate_fused(q_pad, k_pad, v_pad, mask, B, N, H, d, max_seqlen_hint, softmax_scale,
                          dtype, o_pad, cu_seqlens, max_seqlen, &p));
   RVA_TRY(check_i32(work, "work", true));
+  RVA_TRY(check_persistent_items(B, H));
   if (dtype == RVA_F32)  // the persistent form is built for 16-bit inputs; fp32 keeps one launch
     return enqueue_attend(p, dtype, true, static_cast<hipStream_t>(stream));
   p.work = work;
   return enqueue_attend_persistent(p, dtype, static_cast<hipStream_t>(stream));
+}
+
+int rva_fused_persistent_noalloc(const void* q_pad, const void* k_pad, const void* v_pad,
+                                 const uint8_t* mask, int B, int N, int H, int d,
+                                 int max_seqlen_hint, float softmax_scale, int dtype, void* o_pad,
+                                 int32_t* cu_seqlens, int32_t* max_seqlen, void* stream) {
+  rva::AttnParams p;
+  RVA_TRY(validate_fused(q_pad, k_pad, v_pad, mask, B, N, H, d, max_seqlen_hint, softmax_scale,
+                         dtype, o_pad, cu_seqlens, max_seqlen, &p));
+  RVA_TRY(check_persistent_items(B, H));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == RVA_F32)  // as rva_fused_persistent: fp32 runs the one-launch kernel, no counter
+    return enqueue_attend(p, dtype, true, s);
+  RVA_TRY(ensure_init());
+  RVA_TRY(scratch_counter(s, &p.work));
+  return enqueue_attend_persistent(p, dtype, s);
 }
 
 int rva_empty(int count, void* stream) {
@@ -602,6 +693,7 @@ int rva_plan_create(const rva_plan_desc* desc, rva_plan* out) {
       RVA_TRY(validate_fused(D.q_pad, D.k_pad, D.v_pad, D.mask, D.B, D.N, D.H, D.d,
                              D.max_seqlen_hint, D.softmax_scale, D.dtype, D.o_pad, D.cu_seqlens,
                              D.max_seqlen, &attn));
+      RVA_TRY(check_persistent_items(D.B, D.H));
       break;
     case RVA_PLAN_L2_FUSED:
       RVA_TRY(validate_threshold(D.x, D.B, D.N, D.C, D.x_dtype, D.keep_quantile, D.mask_out,

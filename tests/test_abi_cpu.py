@@ -34,7 +34,7 @@ def test_header_lists_the_entry_points():
                  "rva_plan_launch", "rva_plan_destroy", "rva_empty", "rva_status_string",
                  "rva_last_error", "rva_version", "rva_threshold_l2_mask",
                  "rva_qkv_projection", "rva_out_projection", "rva_layers_plan_create",
-                 "rva_fused_persistent"):
+                 "rva_fused_persistent", "rva_fused_persistent_noalloc"):
         assert want in names
 
 
@@ -183,3 +183,20 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(rva, "_lib", None)
     with pytest.raises(ImportError):
         rva.lib()
+
+
+def test_persistent_item_limit(L):
+    """B*H >= 2^30 would wrap the persistent form's 32-bit work counter: both
+    persistent entry points reject it by host arithmetic, before any HIP
+    call (none can succeed here without a GPU, so reaching one would show as
+    a different error)."""
+    f = ctypes.c_float(0.0)
+    st = L.rva_fused_persistent(FAKE, FAKE, FAKE, FAKE, 1 << 24, 1, 64, 64, 0, f, 1, FAKE, None,
+                                None, FAKE, None)
+    assert st == -1 and b"counter" in L.rva_last_error()
+    st = L.rva_fused_persistent_noalloc(FAKE, FAKE, FAKE, FAKE, 1 << 24, 1, 64, 64, 0, f, 1, FAKE,
+                                        None, None, None)
+    assert st == -1 and b"counter" in L.rva_last_error()
+    st = L.rva_fused_persistent_noalloc(FAKE, FAKE, FAKE, None, 4, 8, 2, 64, 0, f, 1, FAKE,
+                                        None, None, None)
+    assert st == -1 and b"mask" in L.rva_last_error()
