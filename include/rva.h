@@ -92,11 +92,16 @@ int rva_pack(const void* q_pad, const void* k_pad, const void* v_pad, const uint
  *
  * For every image b and head h: O = softmax(Q K^T * scale) V over rows
  * cu[b]..cu[b+1]-1 of q/k/v ([T,H,d]), written to o ([T,H,d], capacity T).
- *   max_seqlen : host-side upper bound on every n_b.  It only sizes the
- *                on-chip staging; any value >= 1 gives correct results
- *                (longer sequences are streamed in chunks), the true maximum
- *                gives the best speed.  <= 0 selects the largest chunk.
- * One kernel launch of B*H workgroups.
+ *   max_seqlen : host-side bound on every n_b, at most RVA_MAX_TOKENS.  It
+ *                only sizes the on-chip staging and the launch; any value
+ *                >= 1 gives correct results (longer sequences are streamed
+ *                in chunks), the true maximum gives the best speed.  <= 0
+ *                means RVA_MAX_TOKENS.
+ * Every n_b must be at most RVA_MAX_TOKENS (the offsets are device data and
+ * are not read on the host): a longer sequence is outside the contract and
+ * its output rows are left unwritten.
+ * One kernel launch: a workgroup per (sequence, head), or per query tile of
+ * one when that leaves compute units idle (rva_set_query_split).
  */
 int rva_ragged_attend(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
                       int B, int H, int d, int max_seqlen, float softmax_scale, int dtype,
@@ -351,6 +356,25 @@ typedef struct {
 #define RVA_MAX_LAYERS 64
 
 int rva_layers_plan_create(const rva_layers_desc* desc, rva_plan* out);
+
+/*
+ * rva_set_query_split -- how the attention launches of this process split
+ * each (sequence, head) into query tiles, one workgroup per tile.  The
+ * default, 0, lets every launch choose from the device's compute units and
+ * its length bound: fp32 takes one tile per 16-query block; 16-bit launches
+ * with fewer (sequence, head) items than resident workgroup slots take as
+ * many tiles as fill the slots (at most one 16-query block per wave), and
+ * larger ones one workgroup per (sequence, head), or per head pair.
+ * split >= 1 forces that many tiles (at most one per 16-query block of the
+ * length bound; 1 also turns head pairing off) on every later launch and
+ * plan creation, except the persistent forms.  It exists for tests and
+ * tuning: results stay within the same error bounds, identical bit for bit
+ * for fp32 and for 16-bit sequences staged whole; a sequence streamed in key
+ * chunks may differ in its last bits, because the chunk order of a query
+ * block depends on which pass of its workgroup runs it.  RVA_ERR_INVALID
+ * for split < 0.
+ */
+int rva_set_query_split(int split);
 
 /*
  * rva_empty -- enqueue `count` launches of an empty one-workgroup kernel on

@@ -17,7 +17,7 @@ import torch
 
 __all__ = ["RVAError", "lib", "pack", "ragged_attend", "unpack", "fused", "threshold_l2_mask",
            "qkv_projection", "out_projection", "index", "LayersPlan", "fused_persistent",
-           "fused_persistent_noalloc",
+           "fused_persistent_noalloc", "set_query_split",
            "PERSISTENT",
            "Plan", "empty", "dtype_code", "F32", "F16", "BF16", "STAGED", "FUSED", "EMPTY",
            "L2_FUSED", "MAX_TOKENS"]
@@ -90,6 +90,7 @@ def lib() -> ctypes.CDLL:
     L.rva_layers_plan_create.argtypes = [ctypes.POINTER(_LayersDesc), ctypes.POINTER(ctypes.c_void_p)]
     L.rva_plan_destroy.argtypes = [P]
     L.rva_empty.argtypes = [I, P]
+    L.rva_set_query_split.argtypes = [I]
     L.rva_threshold_l2_mask.argtypes = [P, I, I, I, I, ctypes.c_double, P, P]
     L.rva_qkv_projection.argtypes = [P, P, P, I, I, I, P, P, I, P, P, P, P]
     L.rva_out_projection.argtypes = [P, P, P, P, I, I, I, P, P, P, I, P, P]
@@ -102,7 +103,7 @@ def lib() -> ctypes.CDLL:
                  "rva_plan_launch", "rva_plan_destroy", "rva_empty", "rva_version",
                  "rva_threshold_l2_mask", "rva_qkv_projection", "rva_out_projection",
                  "rva_layers_plan_create", "rva_fused_persistent",
-                 "rva_fused_persistent_noalloc"):
+                 "rva_fused_persistent_noalloc", "rva_set_query_split"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -185,20 +186,43 @@ def _mask_u8(mask, B=None, N=None):
     return mask
 
 
+def _like(t, dev: int, dtype, shape) -> bool:
+    """Fast form of the checks: `t` is a contiguous tensor on device `dev`
+    with this dtype and shape (False for anything else, non-tensors
+    included).  Callers re-run _dev on failure to word the error."""
+    try:
+        return (t.get_device() == dev and t.dtype == dtype and t.shape == shape
+                and t.is_contiguous())
+    except AttributeError:
+        return False
+
+
 def _qkv(q, k, v):
-    """Padded q/k/v: [B, N, H, 64] of one supported dtype, identical shapes."""
+    """Padded q/k/v: [B, N, H, 64] of one supported dtype, identical shapes.
+    Returns (shape, device index)."""
     _dev(q, "q")
-    if q.dim() != 4 or q.shape[3] != HEAD_DIM:
-        raise ValueError(f"q must be [B, N, H, {HEAD_DIM}] (got {tuple(q.shape)})")
+    sh = q.shape
+    if len(sh) != 4 or sh[3] != HEAD_DIM:
+        raise ValueError(f"q must be [B, N, H, {HEAD_DIM}] (got {tuple(sh)})")
     dtype_code(q)
-    _dev(k, "k", dtype=q.dtype, shape=q.shape)
-    _dev(v, "v", dtype=q.dtype, shape=q.shape)
-    return tuple(q.shape)
+    dev = q.get_device()
+    for name, t in (("k", k), ("v", v)):
+        if not _like(t, dev, q.dtype, sh):
+            _dev(t, name, dtype=q.dtype, shape=sh)
+            raise ValueError(f"{name} must be on the device of q")
+    return sh, dev
 
 
-def _offsets(cu_seqlens, max_seqlen, B):
-    _opt(cu_seqlens, "cu_seqlens", dtype=torch.int32, shape=(B + 1,))
-    _opt(max_seqlen, "max_seqlen", dtype=torch.int32, numel=1)
+_I32 = torch.int32
+
+
+def _offsets(cu_seqlens, max_seqlen, B, dev=None):
+    if cu_seqlens is not None and not (dev is not None and _like(cu_seqlens, dev, _I32, (B + 1,))):
+        _dev(cu_seqlens, "cu_seqlens", dtype=_I32, shape=(B + 1,))
+    if max_seqlen is not None and not (dev is not None and max_seqlen.get_device() == dev and
+                                       max_seqlen.dtype == _I32 and max_seqlen.numel() >= 1 and
+                                       max_seqlen.is_contiguous()):
+        _dev(max_seqlen, "max_seqlen", dtype=_I32, numel=1)
 
 
 def pack(q, k, v, mask, *, outputs=None, kept_index=True, stream=None):
@@ -317,13 +341,53 @@ def unpack(o_packed, cu_seqlens, mask, *, out=None, stream=None):
     return out
 
 
+_U8 = torch.uint8
+_MIN_DEV = 0  # device indices of GPU tensors (CPU tensors report -1)
+
+
+def _fused_fast(q, k, v, mask, out, cu, mx) -> bool:
+    """The checks of _fused_args as one expression (no calls, for the
+    per-call path): every tensor on q's device, which is the current one,
+    contiguous, of the expected dtype and shape.  False sends the caller
+    through the detailed checks, which word the error."""
+    try:
+        sh = q.shape
+        dt = q.dtype
+        dev = q.get_device()
+        return (dev >= _MIN_DEV and len(sh) == 4 and sh[3] == HEAD_DIM and dt in _DTYPES
+                and q.is_contiguous()
+                and k.get_device() == dev and k.dtype == dt and k.shape == sh and k.is_contiguous()
+                and v.get_device() == dev and v.dtype == dt and v.shape == sh and v.is_contiguous()
+                and mask.get_device() == dev and mask.dtype == _U8 and mask.shape == sh[:2]
+                and mask.is_contiguous()
+                and (out is None or (out.get_device() == dev and out.dtype == dt
+                                     and out.shape == sh and out.is_contiguous()))
+                and (cu is None or (cu.get_device() == dev and cu.dtype == _I32
+                                    and cu.shape == (sh[0] + 1,) and cu.is_contiguous()))
+                and (mx is None or (mx.get_device() == dev and mx.dtype == _I32
+                                    and mx.numel() >= 1 and mx.is_contiguous()))
+                and (_cur_device is None or dev == _cur_device()))
+    except AttributeError:
+        return False
+
+
 def _fused_args(q, k, v, mask, out, cu_seqlens, max_seqlen):
-    B, N, H, d = _qkv(q, k, v)
-    m = _mask_u8(mask, B, N)
+    if _fused_fast(q, k, v, mask, out, cu_seqlens, max_seqlen):
+        return mask, (torch.empty_like(q) if out is None else out), tuple(q.shape)
+    sh, dev = _qkv(q, k, v)
+    B, N, H, d = sh
+    if _like(mask, dev, _U8, (B, N)):
+        m = mask
+    else:
+        m = _mask_u8(mask, B, N)
+        if m.get_device() != dev:
+            raise ValueError("mask must be on the device of q")
     if out is None:
         out = torch.empty_like(q)
-    _dev(out, "out", dtype=q.dtype, shape=q.shape)
-    _offsets(cu_seqlens, max_seqlen, B)
+    elif not _like(out, dev, q.dtype, sh):
+        _dev(out, "out", dtype=q.dtype, shape=sh)
+        raise ValueError("out must be on the device of q")
+    _offsets(cu_seqlens, max_seqlen, B, dev)
     return m, out, (B, N, H, d)
 
 
@@ -457,6 +521,12 @@ def out_projection(o, cu_seqlens, w_o, b_o=None, *, kept_index=None, mask=None, 
                                     _ptr(w_o), _ptr(b_o), _ptr(residual), dtype_code(o), _ptr(out),
                                     _stream(stream)), "rva_out_projection")
     return out
+
+
+def set_query_split(split: int):
+    """Query tiles per (sequence, head) on every later attention launch of
+    this process (0: each launch chooses; results never depend on it)."""
+    _check(lib().rva_set_query_split(int(split)), "rva_set_query_split")
 
 
 def empty(count: int = 1, stream=None):

@@ -105,42 +105,12 @@ __device__ __forceinline__ float max8(f32x4 a, f32x4 b) {
 constexpr float kRescaleSlack = 8.0f;  // log2 units: probabilities stay <= 2^8
 
 // Online-softmax update for one 16-query block and one 32-key tile whose
-// scores are s0 (keys 4g..4g+3) and s1 (keys 16+4g..16+4g+3) in this lane.
-// Writes the (unnormalised) probabilities to pr[8]; rescales `o` and `l`
-// only when some query's max grew by more than kRescaleSlack.
-__device__ __forceinline__ void softmax_step(f32x4& s0, f32x4& s1, int kvalid, float c, float& m,
-                                             float& l, f32x4 (&o)[4], float (&pr)[8]) {
-  const int g = lane_id() >> 4;
-  if (kvalid < kKeyTile) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (4 * g + j >= kvalid) s0[j] = -INFINITY;
-      if (16 + 4 * g + j >= kvalid) s1[j] = -INFINITY;
-    }
-  }
-  const float mt = quad_max(max8(s0, s1)) * c;
-  if (__any(mt > m + kRescaleSlack)) {
-    const float mnew = fmaxf(m, mt);
-    const float alpha = fast_exp2(m - mnew);
-    m = mnew;
-    l *= alpha;
-#pragma unroll
-    for (int db = 0; db < 4; ++db) o[db] *= alpha;
-  }
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    pr[j] = fast_exp2(fmaf(s0[j], c, -m));
-    pr[4 + j] = fast_exp2(fmaf(s1[j], c, -m));
-  }
-  float sum = 0.f;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) sum += pr[j];
-  l += sum;
-}
-
-// 16-bit variant: the row sums are a fifth accumulator block o[4] (computed
-// by the matrix cores from an all-ones operand), so only the max is tracked
-// here; a rescale multiplies all five blocks.
+// scores are s0 (keys 4g..4g+3) and s1 (keys 16+4g..16+4g+3) in this lane:
+// writes the (unnormalised) probabilities to pr[8] and rescales the
+// accumulators only when some query's max grew by more than kRescaleSlack.
+// The row sums are a fifth accumulator block o[4] (computed by the matrix
+// cores from an all-ones operand), so only the max is tracked here; a
+// rescale multiplies all five blocks.
 __device__ __forceinline__ void softmax_step16(f32x4& s0, f32x4& s1, int kvalid, float c, float& m,
                                                f32x4 (&o)[5], float (&pr)[8]) {
   const int g = lane_id() >> 4;
@@ -457,10 +427,13 @@ __device__ __forceinline__ void stage16(Rsrc rk, Rsrc rv, unsigned char* Ks, uns
 // `last_use()` is called by every thread once, right after the sequence's
 // kept-row list (through roff) has been read for the last time: at the last
 // chunk of the last pass, before its multiply.
+// The workgroup takes the query blocks qt, qt + qs, qt + 2 qs, ... of the
+// sequence (all of them when qs = 1); a launch that splits each sequence
+// into qs query tiles gives tile qt to one workgroup.
 template <int DT, typename RowOff, typename Hook>
 __device__ __forceinline__ void attend_seq16(const AttnParams& p, int n, unsigned char* kvbase,
                                              Rsrc rq, Rsrc rk, Rsrc rv, Rsrc ro, RowOff roff,
-                                             Hook last_use) {
+                                             Hook last_use, int qt = 0, int qs = 1) {
   typedef Half16<DT> Tr;
   typedef typename Tr::V8 V8;
   const int lane = lane_id(), w = wave_id(), g = lane >> 4, r16 = lane & 15;
@@ -470,7 +443,8 @@ __device__ __forceinline__ void attend_seq16(const AttnParams& p, int n, unsigne
   constexpr int kWaves = kAttnThreads16 / 64;
   constexpr int kPerPass = kWaves * kQBlocksPerWave;
   const int nqb = (n + kQBlock - 1) / kQBlock;
-  const int npass = (nqb + kPerPass - 1) / kPerPass;
+  const int nqt = qt < nqb ? (nqb - qt + qs - 1) / qs : 0;  // this workgroup's blocks
+  const int npass = (nqt + kPerPass - 1) / kPerPass;
   const int nchunk = (n + kc - 1) / kc;
   const float c = p.scale_log2e;
 
@@ -484,8 +458,8 @@ __device__ __forceinline__ void attend_seq16(const AttnParams& p, int n, unsigne
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       qb[i] = pass * kPerPass + w + i * kWaves;
-      act[i] = qb[i] < nqb;
-      const int q = qb[i] * kQBlock + r16;
+      act[i] = qb[i] < nqt;
+      const int q = (qt + qs * qb[i]) * kQBlock + r16;
       qoff[i] = (act[i] && q < n) ? roff(q) : kOOB;
       // B operand of S^T = K Q^T: lane (r16, g) holds Q[q][32 ks + 8 g .. + 7]
       qf[i][0] = __builtin_bit_cast(V8, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)(qoff[i] + 16 * g), 0, 0));
@@ -548,10 +522,12 @@ constexpr int kQSlots = 3;
 // an opaque move, so they are not hoisted) instead of holding them across
 // the tile loops; for callers whose own live state leaves no registers for
 // them, where they would otherwise be spilled and reloaded every tile.
+// The units are the (head, query block) pairs of the workgroup's query
+// blocks qt, qt + qs, ... (qt < the sequence's block count).
 template <int DT, bool LANES_PER_TILE = false, typename RowOff, typename Hook>
 __device__ __forceinline__ void attend_resident16(int n, int nh, float c, unsigned char* kvbase,
                                                   Rsrc rq, Rsrc rk, Rsrc rv, Rsrc ro, RowOff roff,
-                                                  Hook last_use) {
+                                                  Hook last_use, int qt = 0, int qs = 1) {
   typedef Half16<DT> Tr;
   typedef typename Tr::V8 V8;
   constexpr int kWaves = kAttnThreads16 / 64;
@@ -564,14 +540,15 @@ __device__ __forceinline__ void attend_resident16(int n, int nh, float c, unsign
   const int lane = lane_id(), w = wave_id(), g = lane >> 4, r16 = lane & 15;
   const int rows = round_up(n, kQBlock);  // staged rows per head, K and V each
   const int nqb = rows / kQBlock;
-  const int nunits = nh * nqb;
+  const int nqt = (nqb - qt + qs - 1) / qs;  // the workgroup's query blocks per head
+  const int nunits = nh * nqt;
   // every kept-row offset is read before the staging barrier
   uint32_t qoff[kUnitsPerWave];
 #pragma unroll
   for (int i = 0; i < kUnitsPerWave; ++i) {
     const int u = w + i * kWaves;
-    const int hu = u / nqb;
-    const int q = (u - hu * nqb) * kQBlock + r16;
+    const int hu = u / nqt;
+    const int q = (qt + qs * (u - hu * nqt)) * kQBlock + r16;
     qoff[i] = (u < nunits && q < n) ? roff(q) + (uint32_t)hu * kHeadBytes : kOOB;
   }
   auto load_q = [&](uint32_t off, V8 (&qs)[2]) {
@@ -607,7 +584,7 @@ __device__ __forceinline__ void attend_resident16(int n, int nh, float c, unsign
     if (u >= nunits) break;
     const int slot = i % kQSlots;
     if (i == 1 && w + kQSlots * kWaves < nunits) load_q(qoff[kQSlots], qf[0]);
-    const int hu = u / nqb;
+    const int hu = u / nqt;
     const unsigned char* Ks = kvbase + hu * rows * 2 * kHeadBytes;
     const unsigned char* Vs = Ks + rows * kHeadBytes;
     // The block's softmax runs against a fixed reference max: the first
@@ -691,158 +668,144 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// fp32 matrix-core form.  The 16x16x4 product takes one k value per lane
-// group; lane group g covers head dims 16g..16g+15 over 16 steps (any
-// consistent split of the contraction is valid), so each lane's Q and K
-// slices are 64 contiguous bytes.  For P V the k index is the key: step
-// (kb, j) uses key 16kb + 4g + j, which is exactly the score this lane holds.
-__device__ __forceinline__ void tile32(const float* __restrict__ Ks, const float* __restrict__ Vs,
-                                       int k0, int kvalid, const f32x4 (&qf)[2][4],
-                                       f32x4 (&o)[2][4], float (&m)[2], float (&l)[2], bool two,
-                                       float c) {
-  const int lane = lane_id(), g = lane >> 4, r16 = lane & 15;
-  f32x4 kf[2][4];
+__device__ __forceinline__ float max4(f32x4 a) { return fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3])); }
+
+// fp32 inputs: one workgroup per (sequence, head, query tile), the tile's
+// 16-query blocks taken one at a time.  For one block, the workgroup's
+// waves split the keys 16 at a time (wave w: keys 16 w, 16 (w + W), ...),
+// each keeping its own running max, row sum and partial O, which are
+// combined through LDS once every key is seen.  At these lengths one
+// block's keys then take at most a few 16-key steps per wave, so a block
+// costs little more than its memory round trips; the fp32 matrix-core rate
+// (a quarter of the 16-bit one per cycle and operand) would otherwise make
+// a whole sequence per workgroup a long serial chain.
+//
+// Products, 16x16x4 fp32 matrix cores, scores transposed (S^T = K Q^T):
+// step t contracts head dims 16 g + t for lane group g, so lane (r16, g)
+// holds K[key r16][16 g .. 16 g + 15] and Q[query r16][16 g .. + 15] as four
+// 16-byte pieces each, and ends with S[query r16][keys 4 g .. 4 g + 3].  For
+// O^T = V^T P^T, step j contracts keys 4 g + j: lane (r16, g) gives
+// V[key 4 g + j][16 db + r16] (one float per lane, 64 contiguous bytes per
+// 16 lanes) and its own probability P[r16][4 g + j], and ends with
+// O[query r16][16 db + 4 g .. + 3].  K, V and Q come straight from memory
+// through buffer descriptors (rows at or past n read as zeros); nothing is
+// staged in LDS but the combine.
+constexpr int kSlice32 = 16;  // keys per wave step
+constexpr int kWaves32 = kAttnThreads32 / 64;
+
+// One 16-query block (rows 16 qb .. 16 qb + 15 of the sequence).  roff(r) is
+// the byte offset of sequence row r from the descriptors' base.  Two
+// workgroup barriers; every thread must call it.
+template <typename RowOff>
+__device__ __forceinline__ void block32(Rsrc rq, Rsrc rk, Rsrc rv, Rsrc ro, int n, int qb, float c,
+                                        RowOff roff, float* comb) {
+  const int lane = lane_id(), w = wave_id(), g = lane >> 4, r16 = lane & 15;
+  const int q = qb * kQBlock + r16;
+  const uint32_t qoff = q < n ? roff(q) : kOOB;
+  f32x4 qf[4];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+  for (int t4 = 0; t4 < 4; ++t4)
+    qf[t4] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           rq, (int)(qoff + 64 * g + 16 * t4), 0, 0));
+  float m = -INFINITY, l = 0.f;
+  f32x4 o[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int k0 = w * kSlice32; k0 < n; k0 += kWaves32 * kSlice32) {
+    const int kr = k0 + r16;
+    const uint32_t koff = kr < n ? roff(kr) : kOOB;
+    f32x4 kf[4];
 #pragma unroll
     for (int t4 = 0; t4 < 4; ++t4)
-      kf[kb][t4] = *reinterpret_cast<const f32x4*>(Ks + (k0 + kb * 16 + r16) * kPitch32 + 16 * g + 4 * t4);
-  float va[4][8];
+      kf[t4] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                             rk, (int)(koff + 64 * g + 16 * t4), 0, 0));
+    float va[4][4];  // [db][j]: V[k0 + 4 g + j][16 db + r16]
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+    for (int j = 0; j < 4; ++j) {
+      const int vr = k0 + 4 * g + j;
+      const uint32_t voff = vr < n ? roff(vr) : kOOB;
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      va[db][j] = Vs[(k0 + (j >> 2) * 16 + 4 * g + (j & 3)) * kPitch32 + db * 16 + r16];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    if (i == 1 && !two) break;
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      s0 = mfma_f32(kf[0][t >> 2][t & 3], qf[i][t >> 2][t & 3], s0);
-      s1 = mfma_f32(kf[1][t >> 2][t & 3], qf[i][t >> 2][t & 3], s1);
+      for (int db = 0; db < 4; ++db)
+        va[db][j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                  rv, (int)(voff + 4 * (16 * db + r16)), 0, 0));
     }
-    float pr[8];
-    softmax_step(s0, s1, kvalid, c, m[i], l[i], o[i], pr);
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < 16; ++t) s = mfma_f32(kf[t >> 2][t & 3], qf[t >> 2][t & 3], s);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (k0 + 4 * g + j >= n) s[j] = -INFINITY;
+    // key k0 is always valid and lies in lane group 0, so mt is finite
+    const float mt = quad_max(max4(s)) * c;
+    const float mn = fmaxf(m, mt);
+    const float alpha = fast_exp2(m - mn);  // 0 on the first step (m = -inf)
+    m = mn;
+    l *= alpha;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) o[db] *= alpha;
+    float p[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      p[j] = fast_exp2(fmaf(s[j], c, -m));
+      l += p[j];
+    }
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) o[i][db] = mfma_f32(va[db][j], pr[j], o[i][db]);
+      for (int j = 0; j < 4; ++j) o[db] = mfma_f32(va[db][j], p[j], o[db]);
   }
-}
-
-template <typename Elem>
-__device__ __forceinline__ void stage32(const float* __restrict__ kg, const float* __restrict__ vg,
-                                        float* Ks, float* Vs, int c0, int rows, Elem elem) {
-  constexpr int NT = kAttnThreads32;
-  const int tid = threadIdx.x;
-  const int total = round_up(rows, kKeyTile) * 16;  // <= kKcMax32 * 16
-  u32x4 kr[4], vr[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int e = tid + u * NT;
-    kr[u] = u32x4{0u, 0u, 0u, 0u};
-    vr[u] = kr[u];
-    const int r = e >> 4, pc = e & 15;
-    if (e < total && r < rows) {
-      const uint32_t el = elem(c0 + r) + pc * 4;
-      kr[u] = *reinterpret_cast<const u32x4*>(kg + el);
-      vr[u] = *reinterpret_cast<const u32x4*>(vg + el);
-    }
+  l = quad_sum(l);
+  float* cm = comb;                         // [W][16] running maxima
+  float* cl = comb + kWaves32 * 16;         // [W][16] row sums
+  float* co = comb + 2 * kWaves32 * 16;     // [W][16][kCombPitch32] partial O
+  if (g == 0) {
+    cm[w * 16 + r16] = m;
+    cl[w * 16 + r16] = l;
   }
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int e = tid + u * NT;
-    if (e < total) {
-      const int r = e >> 4, pc = e & 15;
-      *reinterpret_cast<u32x4*>(Ks + r * kPitch32 + pc * 4) = kr[u];
-      *reinterpret_cast<u32x4*>(Vs + r * kPitch32 + pc * 4) = vr[u];
-    }
+  for (int db = 0; db < 4; ++db)
+    *reinterpret_cast<f32x4*>(co + (w * 16 + r16) * kCombPitch32 + 16 * db + 4 * g) = o[db];
+  __syncthreads();
+  // thread: query tid / 32, head dims 2 (tid % 32) and the next
+  const int qq = threadIdx.x >> 5, dd = 2 * (threadIdx.x & 31);
+  float M = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < kWaves32; ++i) M = fmaxf(M, cm[i * 16 + qq]);
+  float den = 0.f, n0 = 0.f, n1 = 0.f;
+#pragma unroll
+  for (int i = 0; i < kWaves32; ++i) {
+    const float mi = cm[i * 16 + qq];
+    // a wave that saw no key holds m = -inf, l = 0 and O = 0
+    const float a = mi == -INFINITY ? 0.f : fast_exp2(mi - M);
+    const float* row = co + (i * 16 + qq) * kCombPitch32 + dd;
+    den = fmaf(a, cl[i * 16 + qq], den);
+    n0 = fmaf(a, row[0], n0);
+    n1 = fmaf(a, row[1], n1);
   }
-}
-
-template <typename Elem>
-__device__ __forceinline__ void attend_seq32(const AttnParams& p, int n, unsigned char* kvbase,
-                                             Elem elem) {
-  const int lane = lane_id(), w = wave_id(), g = lane >> 4, r16 = lane & 15;
-  const int kc = p.kc;
-  float* Ks = reinterpret_cast<float*>(kvbase);
-  float* Vs = Ks + kc * kPitch32;
-  const float* __restrict__ qg = static_cast<const float*>(p.q);
-  const float* __restrict__ kg = static_cast<const float*>(p.k);
-  const float* __restrict__ vg = static_cast<const float*>(p.v);
-  float* __restrict__ og = static_cast<float*>(p.o);
-  constexpr int kWaves = kAttnThreads32 / 64;
-  constexpr int kPerPass = kWaves * kQBlocksPerWave;
-  const int nqb = (n + kQBlock - 1) / kQBlock;
-  const int npass = (nqb + kPerPass - 1) / kPerPass;
-  const int nchunk = (n + kc - 1) / kc;
-  const float c = p.scale_log2e;
-
-  for (int pass = 0; pass < npass; ++pass) {
-    int qb[2];
-    bool act[2];
-    f32x4 qf[2][4];
-    f32x4 o[2][4];
-    float m[2], l[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      qb[i] = pass * kPerPass + w + i * kWaves;
-      act[i] = qb[i] < nqb;
-      m[i] = -INFINITY;
-      l[i] = 0.f;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) o[i][db] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int q = qb[i] * kQBlock + r16;
-#pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4) qf[i][t4] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (act[i] && q < n) {
-        const uint32_t e = elem(q);
-#pragma unroll
-        for (int t4 = 0; t4 < 4; ++t4) qf[i][t4] = *reinterpret_cast<const f32x4*>(qg + e + 16 * g + 4 * t4);
-      }
-    }
-    for (int ch = 0; ch < nchunk; ++ch) {
-      const int c0 = ch * kc;
-      const int rows = min(kc, n - c0);
-      if (nchunk > 1 || pass == 0) {
-        if (pass > 0 || ch > 0) __syncthreads();
-        stage32(kg, vg, Ks, Vs, c0, rows, elem);
-        __syncthreads();
-      }
-      if (act[0]) {
-        const int ntile = (rows + kKeyTile - 1) / kKeyTile;
-        for (int t = 0; t < ntile; ++t) {
-          const int k0 = t * kKeyTile;
-          tile32(Ks, Vs, k0, min(kKeyTile, rows - k0), qf, o, m, l, act[1], c);
-        }
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      if (!act[i]) continue;
-      const float inv = 1.f / quad_sum(l[i]);
-      const int q = qb[i] * kQBlock + r16;
-      if (q < n) {
-        const uint32_t e = elem(q);
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-          *reinterpret_cast<f32x4*>(og + e + db * 16 + 4 * g) = o[i][db] * inv;
-      }
-    }
+  const int qo = qb * kQBlock + qq;
+  if (qo < n) {
+    const float inv = 1.f / den;
+    u32x2 out;
+    out[0] = __float_as_uint(n0 * inv);
+    out[1] = __float_as_uint(n1 * inv);
+    __builtin_amdgcn_raw_buffer_store_b64(out, ro, (int)(roff(qo) + 4 * dd), 0, 0);
   }
+  __syncthreads();  // the combine area is free for the next block
 }
 
 // ---------------------------------------------------------------- kernels
 
 // Zero the output rows of pruned tokens of one (image, head); `o` points at
-// the head's slice of the image's first token row.
+// the head's slice of the image's first token row.  When `parts`
+// workgroups share the (image, head), this one takes its part `part` of
+// the 16-byte pieces.
 template <int NT, int ESIZE>
-__device__ __forceinline__ void zero_pruned(char* o, const uint64_t* ballots, int N, int H) {
+__device__ __forceinline__ void zero_pruned(char* o, const uint64_t* ballots, int N, int H,
+                                            int part = 0, int parts = 1) {
   constexpr int PIECES = kHeadDim * ESIZE / 16;
   const uint32_t rs = (uint32_t)(H * kHeadDim * ESIZE);
   const int total = N * PIECES;
-  for (int e = threadIdx.x; e < total; e += NT) {
+  for (int e = threadIdx.x + part * NT; e < total; e += parts * NT) {
     const int j = e / PIECES, pc = e - j * PIECES;
     const bool kept = (ballots[j >> 6] >> (j & 63)) & 1ull;
     if (!kept) *reinterpret_cast<u32x4*>(o + (uint32_t)j * rs + pc * 16) = u32x4{0u, 0u, 0u, 0u};
@@ -864,21 +827,38 @@ __device__ __forceinline__ AttnParams rebase(const AttnParams& p, size_t elem0, 
 
 // The work of grid position `bid` of the attention launch: in the fused
 // form an image's head group (or one head of a tail image), in the packed
-// form one (sequence, head).  `hook()` is called by every thread at least
-// once after the item's first staging barrier, or after its zero fill when
-// the image keeps no token (the persistent form hands over its next item
-// index there).
+// form one (sequence, head); with query tiles (p.qsplit = S > 1, and every
+// fp32 launch) one query tile of one (sequence, head).  Tiles are laid out
+// so that the S tiles of item i sit at grid positions congruent to i modulo
+// 8: workgroups are dealt to the 8 XCDs round robin, so all tiles of a
+// sequence run on one XCD and share its K/V rows through that XCD's L2.
+// `hook()` is called by every thread at least once after the item's first
+// staging barrier, or after its zero fill when the image keeps no token
+// (the persistent form, which never splits, hands over its next item index
+// there).
 template <int DT, bool FUSED, bool LANES_PER_TILE = false, typename Hook>
 __device__ __forceinline__ void attend_item(const AttnParams& p, int bid, unsigned char* smem,
                                             Hook hook) {
   constexpr int NT = DT == 0 ? kAttnThreads32 : kAttnThreads16;
-  // fused 16-bit: a workgroup may take several heads of one image in turn,
-  // so that the mask row is read and compacted once for all of them; the
-  // last tail_b images of the batch (dispatched last) take one head per
-  // workgroup, so the launch ends on short workgroups
+  const int S = p.qsplit;
   int HG = (FUSED && DT != 0) ? p.heads_per_wg : 1;
-  int b, hg;
-  {
+  int b, hg, t = 0;
+  if (DT == 0 || S > 1) {
+    const int grp = bid / (8 * S), r = bid - grp * 8 * S;
+    t = r >> 3;
+    const int i = grp * 8 + (r & 7);
+    if (i >= p.B * p.H) {  // padding of the last group of 8 items
+      hook();
+      return;
+    }
+    b = i / p.H;
+    hg = i - b * p.H;
+    HG = 1;
+  } else {
+    // fused 16-bit: a workgroup may take several heads of one image in
+    // turn, so that the mask row is read and compacted once for all of
+    // them; the last tail_b images of the batch (dispatched last) take one
+    // head per workgroup, so the launch ends on short workgroups
     const int ngrp = (p.H + HG - 1) / HG;
     const int lead = (p.B - p.tail_b) * ngrp;
     if (bid < lead) {
@@ -902,21 +882,23 @@ __device__ __forceinline__ void attend_item(const AttnParams& p, int bid, unsign
     unsigned char* kvbase = smem + attn_compact_bytes(N);
     const int h0 = hg * HG, h1 = min(H, h0 + HG);
     const uint32_t bytes = (uint32_t)N * rs * ES;
+    auto roff = [=](int r) -> uint32_t { return (uint32_t)idx[min(r, n - 1)] * (rs * ES); };
     if constexpr (DT != 0) {
       if (n > 0 && n <= p.rc) {
         // whole sequence resident: as many of the group's heads at once as
         // their K/V rows fit in the staging area
         const int fit = p.rc / round_up(n, kQBlock);
-        auto roff = [=](int r) -> uint32_t { return (uint32_t)idx[min(r, n - 1)] * (rs * ES); };
         for (int h = h0; h < h1;) {
           const int nh = min(fit, h1 - h);
           if (h > h0) __syncthreads();  // the previous heads' staged rows are consumed
           const AttnParams pl = rebase(p, ((size_t)b * N * H + h) * kHeadDim, ES);
           for (int j = 0; j < nh; ++j)
-            zero_pruned<NT, ES>(static_cast<char*>(pl.o) + j * kHeadDim * ES, ballots, N, H);
-          attend_resident16<DT, LANES_PER_TILE>(n, nh, p.scale_log2e, kvbase, make_rsrc(pl.q, bytes),
-                                make_rsrc(pl.k, bytes), make_rsrc(pl.v, bytes),
-                                make_rsrc(pl.o, bytes), roff, hook);
+            zero_pruned<NT, ES>(static_cast<char*>(pl.o) + j * kHeadDim * ES, ballots, N, H, t, S);
+          if (t * kQBlock < n)  // the tile has query rows
+            attend_resident16<DT, LANES_PER_TILE>(n, nh, p.scale_log2e, kvbase,
+                                                  make_rsrc(pl.q, bytes), make_rsrc(pl.k, bytes),
+                                                  make_rsrc(pl.v, bytes), make_rsrc(pl.o, bytes),
+                                                  roff, hook, t, S);
           h += nh;
         }
         return;
@@ -925,15 +907,16 @@ __device__ __forceinline__ void attend_item(const AttnParams& p, int bid, unsign
     for (int h = h0; h < h1; ++h) {
       if (h > hg * HG) __syncthreads();  // the previous head's staged rows are consumed
       const AttnParams pl = rebase(p, ((size_t)b * N * H + h) * kHeadDim, ES);
-      zero_pruned<NT, ES>(static_cast<char*>(pl.o), ballots, N, H);
+      zero_pruned<NT, ES>(static_cast<char*>(pl.o), ballots, N, H, t, S);
       if (n <= 0) continue;
-      auto elem = [=](int r) -> uint32_t { return (uint32_t)idx[r] * rs; };
       if constexpr (DT == 0) {
-        attend_seq32(pl, n, kvbase, elem);
+        float* comb = reinterpret_cast<float*>(kvbase);
+        for (int qb = t; qb * kQBlock < n; qb += S)
+          block32(make_rsrc(pl.q, bytes), make_rsrc(pl.k, bytes), make_rsrc(pl.v, bytes),
+                  make_rsrc(pl.o, bytes), n, qb, p.scale_log2e, roff, comb);
       } else {
-        auto roff = [=](int r) -> uint32_t { return (uint32_t)idx[min(r, n - 1)] * (rs * ES); };
         attend_seq16<DT>(pl, n, kvbase, make_rsrc(pl.q, bytes), make_rsrc(pl.k, bytes),
-                         make_rsrc(pl.v, bytes), make_rsrc(pl.o, bytes), roff, hook);
+                         make_rsrc(pl.v, bytes), make_rsrc(pl.o, bytes), roff, hook, t, S);
       }
     }
     if (n <= 0) hook();
@@ -941,21 +924,27 @@ __device__ __forceinline__ void attend_item(const AttnParams& p, int bid, unsign
     const int h = hg;
     const int row0 = p.cu[b];
     const int n = p.cu[b + 1] - row0;
-    if (n <= 0) return;
+    // sequences longer than the ABI's token limit are outside the contract:
+    // their rows are left as they are (offsets then stay within 32 bits)
+    if (n <= 0 || n > kMaxSeq) return;
     const AttnParams pl = rebase(p, ((size_t)row0 * H + h) * kHeadDim, ES);
-    auto elem = [=](int r) -> uint32_t { return (uint32_t)r * rs; };
+    const uint32_t bytes = (uint32_t)n * rs * ES;
+    auto roff = [=](int r) -> uint32_t { return (uint32_t)r * (rs * ES); };
     if constexpr (DT == 0) {
-      attend_seq32(pl, n, smem, elem);
+      float* comb = reinterpret_cast<float*>(smem);
+      for (int qb = t; qb * kQBlock < n; qb += S)
+        block32(make_rsrc(pl.q, bytes), make_rsrc(pl.k, bytes), make_rsrc(pl.v, bytes),
+                make_rsrc(pl.o, bytes), n, qb, p.scale_log2e, roff, comb);
     } else {
-      const uint32_t bytes = (uint32_t)n * rs * ES;
-      auto roff = [=](int r) -> uint32_t { return (uint32_t)r * (rs * ES); };
-      if (n <= p.rc)
-        attend_resident16<DT>(n, 1, p.scale_log2e, smem, make_rsrc(pl.q, bytes),
-                              make_rsrc(pl.k, bytes), make_rsrc(pl.v, bytes),
-                              make_rsrc(pl.o, bytes), roff, hook);
-      else
+      if (n <= p.rc) {
+        if (t * kQBlock < n)
+          attend_resident16<DT>(n, 1, p.scale_log2e, smem, make_rsrc(pl.q, bytes),
+                                make_rsrc(pl.k, bytes), make_rsrc(pl.v, bytes),
+                                make_rsrc(pl.o, bytes), roff, hook, t, S);
+      } else {
         attend_seq16<DT>(pl, n, smem, make_rsrc(pl.q, bytes), make_rsrc(pl.k, bytes),
-                         make_rsrc(pl.v, bytes), make_rsrc(pl.o, bytes), roff, hook);
+                         make_rsrc(pl.v, bytes), make_rsrc(pl.o, bytes), roff, hook, t, S);
+      }
     }
   }
 }
@@ -1061,6 +1050,18 @@ static int resident_rows(int dtype, bool fused, int N, int kc, int reserved) {
 
 static int kv_rows(int dtype, int kc, int rc) { return dtype == 0 ? kc : (rc > kc ? rc : kc); }
 
+int attend_resident_rows(int dtype, bool fused, int N, int kc) {
+  return resident_rows(dtype, fused, N, kc, (fused && dtype != 0) ? kItemSlotBytes : 0);
+}
+
+long long attend_grid_items(const AttnParams& p, int dtype, bool fused) {
+  const long long bh = (long long)p.B * p.H;
+  if (dtype == 0 || p.qsplit > 1) return (bh + 7) / 8 * 8 * p.qsplit;
+  const int hg = (fused && dtype != 0) ? p.heads_per_wg : 1;
+  const int tail = (fused && dtype != 0) ? p.tail_b : 0;
+  return (long long)(p.B - tail) * ((p.H + hg - 1) / hg) + (long long)tail * p.H;
+}
+
 // Dynamic LDS of the fused 16-bit kernels: compaction area, staging area and
 // the persistent form's item slot (reserved by both forms, so that both give
 // the same sequences the same staging).
@@ -1113,9 +1114,7 @@ hipError_t launch_attend(const AttnParams& p0, int dtype, bool fused, hipStream_
   p.rc = resident_rows(dtype, fused, p.N, p.kc, fused16 ? kItemSlotBytes : 0);
   const size_t lds = fused16 ? fused16_lds(p.N, p.kc, p.rc)
                              : attn_lds_bytes(dtype, fused, p.N, kv_rows(dtype, p.kc, p.rc));
-  const int hg = (fused && dtype != 0) ? p.heads_per_wg : 1;
-  const int tail = (fused && dtype != 0) ? p.tail_b : 0;
-  const int grid = (p.B - tail) * ((p.H + hg - 1) / hg) + tail * p.H +
+  const int grid = (int)attend_grid_items(p, dtype, fused) +
                    ((fused && (p.cu_out || p.max_out)) ? 1 : 0);
   const dim3 blk(attn_threads(dtype));
   if (dtype == 0) {

@@ -10,6 +10,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 #include <new>
 #include <vector>
@@ -85,8 +86,8 @@ float resolve_scale(float s, int d) {
   return s * 1.4426950408889634f;  // fold log2(e) so the kernel uses exp2
 }
 
-int pick_kc(int dtype, int hint, int fallback) {
-  const int cap = rva::attn_kc_max(dtype);
+int pick_kc(int hint, int fallback) {
+  const int cap = rva::kKcMax16;
   int n = hint > 0 ? hint : fallback;
   if (n < 1) n = cap;
   int kc = rva::round_up(n, rva::kKeyTile);
@@ -163,6 +164,9 @@ int validate_attend(const void* q, const void* k, const void* v, const int32_t* 
   RVA_TRY(check_data(v, "v", true));
   RVA_TRY(check_data(o, "o", true));
   RVA_TRY(check_i32(cu, "cu_seqlens", true));
+  if (max_seqlen > RVA_MAX_TOKENS)
+    return fail(RVA_ERR_INVALID, "max_seqlen must be at most %d (got %d)", RVA_MAX_TOKENS,
+                max_seqlen);
   memset(p, 0, sizeof(*p));
   p->q = q;
   p->k = k;
@@ -172,7 +176,8 @@ int validate_attend(const void* q, const void* k, const void* v, const int32_t* 
   p->B = B;
   p->N = 0;
   p->H = H;
-  p->kc = pick_kc(dtype, max_seqlen, 0);
+  p->kc = pick_kc(max_seqlen, 0);
+  p->nbound = max_seqlen > 0 ? max_seqlen : RVA_MAX_TOKENS;
   p->scale_log2e = resolve_scale(scale, d);
   return RVA_OK;
 }
@@ -220,7 +225,8 @@ int validate_fused(const void* q, const void* k, const void* v, const uint8_t* m
   p->B = B;
   p->N = N;
   p->H = H;
-  p->kc = pick_kc(dtype, hint > 0 && hint < N ? hint : N, N);
+  p->kc = pick_kc(hint > 0 && hint < N ? hint : N, N);
+  p->nbound = hint > 0 && hint < N ? hint : N;
   p->scale_log2e = resolve_scale(scale, d);
   return RVA_OK;
 }
@@ -376,27 +382,58 @@ int device_cus(int* out) {
   return RVA_OK;
 }
 
-// How the fused 16-bit form groups heads: pairs of an image's heads per
-// workgroup only when the pairs still fill every resident slot (3 per CU)
-// at least twice over; the images dispatched last (about one slot-fill of
-// single heads) stay unpaired.  `items` (if not NULL) receives the number
-// of work items (grid positions, not counting the offsets workgroup).
-int group_heads(rva::AttnParams* p, int dtype, bool fused, long long* items) {
+// Query tiles per (sequence, head) forced on every later launch (0: each
+// launch chooses); rva_set_query_split.
+std::atomic<int> g_query_split{0};
+
+// Work decomposition of an attention launch.  It does not change how an
+// output row is computed in the whole-sequence and fp32 forms (identical
+// bits); in the chunked form a query block's key-chunk order follows its
+// workgroup pass, so its last bits may differ.
+//  - Fused 16-bit launches whose (image, head pair) items fill every
+//    resident slot (3 per CU) at least twice give a workgroup two heads of
+//    one image, so the mask row is read and compacted once for both; the
+//    images dispatched last (about one slot-fill of single heads) stay
+//    unpaired, so the launch ends on short workgroups.
+//  - Launches with fewer (sequence, head) items than resident slots split
+//    each item into S query tiles, one workgroup each: as many tiles as
+//    leave every wave at most one 16-query block (one pass of two blocks in
+//    the chunked form), but no more than the slots need.  Otherwise most
+//    compute units would sit idle while a few run whole sequences.
+//  - fp32 takes one workgroup per 16-query block (its waves split the keys).
+// The persistent form (`persistent`) never splits.  `items` (if not NULL)
+// receives the grid positions of the work items.
+int plan_grid(rva::AttnParams* p, int dtype, bool fused, bool persistent, long long* items) {
   p->heads_per_wg = 1;
   p->tail_b = 0;
-  if (fused && dtype != RVA_F32 && p->H > 1) {
-    int cus = 0;
-    RVA_TRY(device_cus(&cus));
-    const long long slots = 3LL * cus;
-    if ((long long)p->B * ((p->H + 1) / 2) >= 2 * slots) {
-      p->heads_per_wg = 2;
-      const long long t = (slots + p->H - 1) / p->H;
-      p->tail_b = (int)(t < p->B ? t : p->B);
-    }
+  p->qsplit = 1;
+  int cus = 0;
+  RVA_TRY(device_cus(&cus));
+  const long long slots = 3LL * cus;
+  const long long bh = (long long)p->B * p->H;
+  const int nqb = (p->nbound + rva::kQBlock - 1) / rva::kQBlock;  // blocks of the longest sequence
+  const int forced = persistent ? 0 : g_query_split.load(std::memory_order_relaxed);
+  if (dtype == RVA_F32) {
+    p->qsplit = forced > 0 && forced < nqb ? forced : nqb;
+  } else if (forced > 0) {
+    p->qsplit = forced < nqb ? forced : nqb;
+  } else if (fused && p->H > 1 && (long long)p->B * ((p->H + 1) / 2) >= 2 * slots) {
+    p->heads_per_wg = 2;
+    const long long t = (slots + p->H - 1) / p->H;
+    p->tail_b = (int)(t < p->B ? t : p->B);
+  } else if (!persistent && bh < slots) {
+    const int rc = rva::attend_resident_rows(dtype, fused, p->N, p->kc);
+    const bool whole = p->nbound <= rc;
+    const long long per = whole ? (nqb + 3) / 4 : (nqb + 7) / 8;
+    const long long fill = ((whole ? 1 : 2) * slots + bh - 1) / bh;
+    const long long q = per < fill ? per : fill;
+    p->qsplit = q > 1 ? (int)q : 1;
   }
-  const int hg = p->heads_per_wg;
-  if (items)
-    *items = (long long)(p->B - p->tail_b) * ((p->H + hg - 1) / hg) + (long long)p->tail_b * p->H;
+  if (p->qsplit < 1) p->qsplit = 1;
+  const long long n = rva::attend_grid_items(*p, dtype, fused);
+  if (n >= (1ll << 31) - 1)
+    return fail(RVA_ERR_INVALID, "attention launch of %lld workgroups exceeds the grid limit", n);
+  if (items) *items = n;
   return RVA_OK;
 }
 
@@ -416,7 +453,7 @@ int enqueue_attend_persistent(const rva::AttnParams& p0, int dtype, hipStream_t 
   RVA_TRY(ensure_init());
   rva::AttnParams p = p0;
   long long items = 0;
-  RVA_TRY(group_heads(&p, dtype, true, &items));
+  RVA_TRY(plan_grid(&p, dtype, true, true, &items));
   int cus = 0;
   RVA_TRY(device_cus(&cus));
   long long grid = (long long)rva::attend_persistent_per_cu(p.N, p.kc) * cus;
@@ -433,7 +470,7 @@ int enqueue_attend_persistent(const rva::AttnParams& p0, int dtype, hipStream_t 
 int enqueue_attend(const rva::AttnParams& p0, int dtype, bool fused, hipStream_t s) {
   RVA_TRY(ensure_init());
   rva::AttnParams p = p0;
-  RVA_TRY(group_heads(&p, dtype, fused, nullptr));
+  RVA_TRY(plan_grid(&p, dtype, fused, false, nullptr));
   hipError_t e = rva::launch_attend(p, dtype, fused, s);
   if (e != hipSuccess) return hip_fail(e, fused ? "fused launch" : "attention launch");
   return RVA_OK;
@@ -652,6 +689,12 @@ int rva_fused_persistent_noalloc(const void* q_pad, const void* k_pad, const voi
   RVA_TRY(ensure_init());
   RVA_TRY(scratch_counter(s, &p.work));
   return enqueue_attend_persistent(p, dtype, s);
+}
+
+int rva_set_query_split(int split) {
+  if (split < 0) return fail(RVA_ERR_INVALID, "split must be >= 0 (got %d)", split);
+  g_query_split.store(split, std::memory_order_relaxed);
+  return RVA_OK;
 }
 
 int rva_empty(int count, void* stream) {

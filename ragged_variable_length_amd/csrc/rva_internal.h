@@ -17,10 +17,9 @@ constexpr int kKeyTile = 32;        // keys per inner step
 constexpr int kPackThreads = 256;
 constexpr int kScanThreads = 1024;
 
-// Keys staged on chip per chunk.  16-bit: K and V rows [kc][64] halves each
-// (16-byte pieces XOR-swizzled by row); fp32: K and V rows [kc][68] floats.
+// Keys staged on chip per chunk (16-bit forms): K and V rows [kc][64] halves
+// each (16-byte pieces XOR-swizzled by row).  fp32 stages no keys.
 constexpr int kKcMax16 = 192;
-constexpr int kKcMax32 = 128;
 // 16-bit sequences of up to rc rows are staged whole (K and V of one head
 // in one round trip); rc is capped by the registers' query blocks (4 per
 // wave, 4 waves) and by the LDS that keeps 3 workgroups per CU.
@@ -31,7 +30,12 @@ constexpr int kAttnWgPerCu16 = 3;
 // of them): 3 workgroups fit a CU at up to 42 granules (53760 bytes) each.
 constexpr int kLdsGranule = 1280;
 constexpr int kLdsPerWg16 = kLdsPerCu / kAttnWgPerCu16 / kLdsGranule * kLdsGranule;
-constexpr int kPitch32 = 68;   // floats per staged K/V row for fp32
+constexpr int kMaxSeq = 1024;  // longest sequence (= RVA_MAX_TOKENS)
+// fp32 attention: the LDS where the waves' partial results of one 16-query
+// block are combined: per wave 16 maxima, 16 sums and 16 rows of 64 floats
+// (row pitch 68 floats, to spread the rows over the LDS banks).
+constexpr int kCombPitch32 = 68;
+constexpr int kComb32Bytes = (kAttnThreads32 / 64) * (16 + 16 + 16 * kCombPitch32) * 4;
 constexpr int kItemSlotBytes = 16;  // fused 16-bit LDS past the staging area (persistent item slot)
 
 struct AttnParams {
@@ -51,6 +55,8 @@ struct AttnParams {
   int rc;                 // 16-bit: longest sequence staged whole (rows, multiple of 16, >= kc); set at launch
   int tail_b;             // fused 16-bit form: last images taken one head per workgroup (0..B)
   int item_slot;          // persistent form: byte offset of its 4-byte item slot in dynamic LDS; set at launch
+  int qsplit;             // query tiles per (sequence, head): one workgroup each (>= 1; 1 with head pairs)
+  int nbound;             // host: longest sequence the launch is sized for (its length hint)
 };
 
 struct CopyParams {
@@ -89,7 +95,6 @@ struct LinearParams {
 
 __host__ __device__ inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
 
-inline int attn_kc_max(int dtype) { return dtype == 0 ? kKcMax32 : kKcMax16; }
 
 // Compaction area at the start of the fused kernel's LDS: the kept list
 // uint16[N], then one ballot (u64) and one count (int32) per 64-token chunk.
@@ -102,9 +107,10 @@ __host__ __device__ inline size_t attn_compact_bytes(int N) {
 
 inline int attn_threads(int dtype) { return dtype == 0 ? kAttnThreads32 : kAttnThreads16; }
 
-// kv_rows: staged key rows (kc for fp32; max(kc, rc) for 16-bit).
+// kv_rows: staged key rows of the 16-bit forms (max(kc, rc)); fp32 stages
+// nothing but its combine area.
 inline size_t attn_lds_bytes(int dtype, bool fused, int N, int kv_rows) {
-  size_t kv = dtype == 0 ? (size_t)kv_rows * kPitch32 * 4 * 2 : (size_t)kv_rows * kHeadDim * 2 * 2;
+  size_t kv = dtype == 0 ? (size_t)kComb32Bytes : (size_t)kv_rows * kHeadDim * 2 * 2;
   size_t head = fused ? attn_compact_bytes(N) : 0;
   size_t scan = (size_t)(4 * attn_threads(dtype) + 64) * 4;  // fused scan workgroup reuses LDS
   size_t total = head + kv;
@@ -121,6 +127,10 @@ hipError_t launch_attend(const AttnParams& p, int dtype, bool fused, hipStream_t
 // (image, head) items from p.work.
 hipError_t launch_attend_persistent(const AttnParams& p, int dtype, int grid, hipStream_t s);
 int attend_persistent_per_cu(int N, int kc);  // resident workgroups per CU
+// Longest sequence a 16-bit launch stages whole (rows), as launch_attend sets it.
+int attend_resident_rows(int dtype, bool fused, int N, int kc);
+// Grid positions of a launch's work items (without the offsets workgroup).
+long long attend_grid_items(const AttnParams& p, int dtype, bool fused);
 hipError_t launch_empty(hipStream_t s);
 hipError_t attend_init();  // raises the dynamic-LDS limit of every attention kernel
 hipError_t launch_threshold(const ThreshParams& p, int B, int dtype, hipStream_t s);

@@ -185,8 +185,25 @@ RESIDENT_EDGES = [1, 15, 16, 17, 31, 32, 33, 47, 48, 63, 64, 65, 95, 96, 97, 103
                   127, 128, 129, 160, 176, 191, 192, 193, 200, 207, 208, 209, 223, 224, 0]
 
 
+SPLITS = [0, 1, 2, 3, 16]  # 0: the launch chooses; k: k query tiles per (sequence, head)
+
+
+class _split:
+    """Force rva_set_query_split(k) inside the block, back to 0 after."""
+
+    def __init__(self, k):
+        self.k = k
+
+    def __enter__(self):
+        _rva().set_query_split(self.k)
+
+    def __exit__(self, *exc):
+        _rva().set_query_split(0)
+
+
+@pytest.mark.parametrize("split", SPLITS)
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-def test_resident_boundaries(device, dtype):
+def test_resident_boundaries(device, dtype, split):
     """Kept counts on every 16- and 32-row boundary up to the padded length,
     in a batch large enough that the fused form pairs heads (5 heads, so the
     last group has one): sequences staged whole one or two heads at a time,
@@ -197,12 +214,14 @@ def test_resident_boundaries(device, dtype):
     counts = [RESIDENT_EDGES[b % len(RESIDENT_EDGES)] for b in range(B)]
     w = W.random_workload(31 if dtype == "f16" else 32, B=B, N=N, H=H, dtype=dtype,
                           counts=counts, name=f"resident_{dtype}")
-    _say(f"[resident] {dtype} B={B} N={N} H={H}")
+    _say(f"[resident] {dtype} B={B} N={N} H={H} split={split}")
     q, k, v, mask = upload(w, device)
     o = torch.full_like(q, float("nan"))
-    rva.fused(q, k, v, mask, out=o)
     pk = rva.pack(q, k, v, mask)
-    o2 = rva.ragged_attend(pk["q"], pk["k"], pk["v"], pk["cu_seqlens"], N)
+    o2 = torch.full_like(pk["q"], float("nan"))
+    with _split(split):
+        rva.fused(q, k, v, mask, out=o)
+        rva.ragged_attend(pk["q"], pk["k"], pk["v"], pk["cu_seqlens"], N, out=o2)
     torch.cuda.synchronize()
     ref, cu_ref, _, _ = oracle.pack_attend_unpack(w.q, w.k, w.v, w.mask, w.dtype)
     err = max_err(f64(o), ref)
@@ -214,8 +233,9 @@ def test_resident_boundaries(device, dtype):
     assert max_err(f64(o2[:T]), ref_pk) <= TOL[w.dtype]
 
 
+@pytest.mark.parametrize("split", SPLITS)
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-def test_every_length(device, dtype):
+def test_every_length(device, dtype, split):
     """Every kept count from 0 to 224, four images each (900 images, 3
     heads, so the fused form pairs heads and ends on single-head
     workgroups): every exit of the whole-sequence tile loop, every ragged
@@ -227,12 +247,14 @@ def test_every_length(device, dtype):
     B = len(counts)
     w = W.random_workload(33 if dtype == "f16" else 34, B=B, N=N, H=H, dtype=dtype,
                           counts=counts, name=f"every_length_{dtype}")
-    _say(f"[every length] {dtype} B={B} N={N} H={H}")
+    _say(f"[every length] {dtype} B={B} N={N} H={H} split={split}")
     q, k, v, mask = upload(w, device)
     o = torch.full_like(q, float("nan"))
-    rva.fused(q, k, v, mask, out=o, max_seqlen_hint=N)
     pk = rva.pack(q, k, v, mask)
-    o2 = rva.ragged_attend(pk["q"], pk["k"], pk["v"], pk["cu_seqlens"], N)
+    o2 = torch.full_like(pk["q"], float("nan"))
+    with _split(split):
+        rva.fused(q, k, v, mask, out=o, max_seqlen_hint=N)
+        rva.ragged_attend(pk["q"], pk["k"], pk["v"], pk["cu_seqlens"], N, out=o2)
     torch.cuda.synchronize()
     ref, cu_ref, _, _ = oracle.pack_attend_unpack(w.q, w.k, w.v, w.mask, w.dtype)
     err = max_err(f64(o), ref)
@@ -434,3 +456,39 @@ def test_many_images(device, B, N):
     assert int(pk["max_seqlen"].item()) == int(mx_ref)
     assert max_err(f64(o), ref) <= TOL["f16"]
     assert not bits(o)[w.mask == 0].any()
+
+
+@pytest.mark.parametrize("name", ["tiny", "long_f32", "edge_f32", "deit_s_224", "deit_b_384",
+                                  "deit_b_224_p50", "edge_f16", "edge_bf16"])
+def test_split_forms_agree(device, name):
+    """The query-tile split only changes which workgroup computes a query
+    block: for fp32 and for 16-bit sequences staged whole, the fused and
+    packed outputs are identical bit for bit under every forced split, and
+    each matches the oracle."""
+    rva = _rva()
+    w = _get(name)
+    q, k, v, mask = upload(w, device)
+    pk = rva.pack(q, k, v, mask)
+    ref, cu_ref, _, _ = oracle.pack_attend_unpack(w.q, w.k, w.v, w.mask, w.dtype)
+    T = int(cu_ref[-1])
+    ref_pk = ref.reshape(-1, w.H, w.d)[oracle.kept_index(w.mask)]
+    hint = max(int(w.counts.max()), 1)
+    first = None
+    for split in [0, 1, 2, 3, 5, 64]:
+        _say(f"[split] {name} split={split}")
+        with _split(split):
+            o = rva.fused(q, k, v, mask, max_seqlen_hint=hint)
+            o2 = rva.ragged_attend(pk["q"], pk["k"], pk["v"], pk["cu_seqlens"], hint)
+        torch.cuda.synchronize()
+        assert max_err(f64(o), ref) <= TOL[w.dtype]
+        assert max_err(f64(o2[:T]), ref_pk) <= TOL[w.dtype]
+        got = (bits(o), bits(o2[:T]))
+        if first is None:
+            first = got
+        assert np.array_equal(got[0], first[0]) and np.array_equal(got[1], first[1]), split
+
+
+def test_split_setting_rejects_negative(device):
+    rva = _rva()
+    with pytest.raises(rva.RVAError):
+        rva.set_query_split(-1)
