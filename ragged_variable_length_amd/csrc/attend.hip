@@ -138,7 +138,7 @@ __device__ __forceinline__ void softmax_step16(f32x4& s0, f32x4& s1, int kvalid,
 
 // ---------------------------------------------------------------- 16-bit
 
-// Staged K and V are row-major [kc][64] halves (128-byte rows) with the
+// Staged K and V are row-major [rows][64] halves (128-byte rows) with the
 // eight 16-byte pieces of row r stored at slot p ^ (r & 7): the rows one
 // fragment read touches then spread over the banks without padding.
 __device__ __forceinline__ int kvswz(int row, int piece) { return row * 128 + ((piece ^ (row & 7)) << 4); }
@@ -422,14 +422,65 @@ __device__ __forceinline__ void stage16(Rsrc rk, Rsrc rv, unsigned char* Ks, uns
   }
 }
 
-// One sequence (image or packed run), one head.  rq/rk/rv/ro cover the
-// sequence's head slice; roff(r) is the byte offset of its row r.
-// `last_use()` is called by every thread once, right after the sequence's
-// kept-row list (through roff) has been read for the last time: at the last
-// chunk of the last pass, before its multiply.
-// The workgroup takes the query blocks qt, qt + qs, qt + 2 qs, ... of the
-// sequence (all of them when qs = 1); a launch that splits each sequence
-// into qs query tiles gives tile qt to one workgroup.
+// Wait until at most N vector memory operations of this wave are in flight
+// (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left open).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// A workgroup barrier without the memory fence of __syncthreads (which would
+// also wait for the key chunk still in flight): this wave's LDS accesses
+// complete, then s_barrier.  The clobber keeps the compiler from moving
+// memory accesses across it.
+__device__ __forceinline__ void bar_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Streamed form (sequences longer than the whole-sequence staging): keys go
+// through two LDS buffers of kChunk16 rows, and the next chunk's loads are
+// in flight while the current chunk is multiplied.  Every chunk is fetched
+// with the same number of loads per wave (rows past the chunk's end are
+// out-of-range offsets, which land as zeros), so the wait for a chunk is a
+// fixed count of this wave's loads; the last step waits for everything, so
+// no load into LDS is left in flight when the sequence is done.
+constexpr int kChunk16 = 96;
+constexpr int kChunkLoads16 = kChunk16 / 8 / (kAttnThreads16 / 64);  // per wave, K and V each
+static_assert(kChunk16 % (8 * (kAttnThreads16 / 64)) == 0 && kChunk16 % kKeyTile == 0, "chunk shape");
+
+// Stage keys [c0, c0 + rows) (rows <= kChunk16) into Ks / Vs as stage16
+// does: 2 kChunkLoads16 direct-to-LDS loads per wave, always.
+template <typename RowOff>
+__device__ __forceinline__ void stage_chunk16(Rsrc rk, Rsrc rv, unsigned char* Ks,
+                                              unsigned char* Vs, int c0, int rows, RowOff roff) {
+  constexpr int kWaves = kAttnThreads16 / 64;
+  const int lane = lane_id(), w = wave_id();
+  const int rl = lane >> 3;
+  const uint32_t piece16 = (uint32_t)(((lane & 7) ^ rl) << 4);
+  uint32_t off[kChunkLoads16];
+#pragma unroll
+  for (int i = 0; i < kChunkLoads16; ++i) {
+    const int r = 8 * (w + kWaves * i) + rl;
+    off[i] = r < rows ? roff(c0 + r) + piece16 : kOOB;
+  }
+#pragma unroll
+  for (int i = 0; i < kChunkLoads16; ++i) {
+    const int r0 = 8 * (w + kWaves * i);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(Ks + r0 * 128),
+                                             16, off[i], 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(Vs + r0 * 128),
+                                             16, off[i], 0, 0, 0);
+  }
+}
+
+// One sequence (image or packed run), one head, streamed.  rq/rk/rv/ro
+// cover the sequence's head slice; roff(r) is the byte offset of its row r.
+// Each wave carries two 16-query blocks through a pass over every key
+// chunk; the workgroup takes the query blocks qt, qt + qs, qt + 2 qs, ...
+// of the sequence (all of them when qs = 1).  Steps (pass, chunk) run as
+// one sequence: step s computes on buffer s & 1 while step s + 1's chunk
+// lands in the other.  `last_use()` is called by every thread once, after
+// the kept-row list (through roff) has been read for the last time.
 template <int DT, typename RowOff, typename Hook>
 __device__ __forceinline__ void attend_seq16(const AttnParams& p, int n, unsigned char* kvbase,
                                              Rsrc rq, Rsrc rk, Rsrc rv, Rsrc ro, RowOff roff,
@@ -437,69 +488,72 @@ __device__ __forceinline__ void attend_seq16(const AttnParams& p, int n, unsigne
   typedef Half16<DT> Tr;
   typedef typename Tr::V8 V8;
   const int lane = lane_id(), w = wave_id(), g = lane >> 4, r16 = lane & 15;
-  const int kc = p.kc;
-  unsigned char* Ks = kvbase;
-  unsigned char* Vs = kvbase + kc * kHeadDim * 2;
+  constexpr int kBuf = kChunk16 * kHeadDim * 2;  // bytes of K (or V) in one buffer
   constexpr int kWaves = kAttnThreads16 / 64;
   constexpr int kPerPass = kWaves * kQBlocksPerWave;
   const int nqb = (n + kQBlock - 1) / kQBlock;
   const int nqt = qt < nqb ? (nqb - qt + qs - 1) / qs : 0;  // this workgroup's blocks
   const int npass = (nqt + kPerPass - 1) / kPerPass;
-  const int nchunk = (n + kc - 1) / kc;
+  const int nchunk = (n + kChunk16 - 1) / kChunk16;
+  const int nsteps = npass * nchunk;
   const float c = p.scale_log2e;
-
-  for (int pass = 0; pass < npass; ++pass) {
-    int qb[2];
-    bool act[2];
-    uint32_t qoff[2];
-    V8 qf[2][2];
-    f32x4 o[2][5];
-    float m[2];
+  if (nsteps == 0) return;
+  stage_chunk16(rk, rv, kvbase, kvbase + kBuf, 0, min(kChunk16, n), roff);
+  int qb[2];
+  bool act[2];
+  uint32_t qoff[2];
+  V8 qf[2][2];
+  f32x4 o[2][5];
+  float m[2];
+  for (int s = 0; s < nsteps; ++s) {
+    const int pass = s / nchunk, cc = s - pass * nchunk;
+    if (cc == 0) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      qb[i] = pass * kPerPass + w + i * kWaves;
-      act[i] = qb[i] < nqt;
-      const int q = (qt + qs * qb[i]) * kQBlock + r16;
-      qoff[i] = (act[i] && q < n) ? roff(q) : kOOB;
-      // B operand of S^T = K Q^T: lane (r16, g) holds Q[q][32 ks + 8 g .. + 7]
-      qf[i][0] = __builtin_bit_cast(V8, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)(qoff[i] + 16 * g), 0, 0));
-      qf[i][1] = __builtin_bit_cast(V8, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)(qoff[i] + 64 + 16 * g), 0, 0));
-    }
-    for (int cc = 0; cc < nchunk; ++cc) {
-      // odd passes walk the chunks backwards so the chunk left staged by the
-      // previous pass is used first (softmax accumulation is order-free)
-      const int ch = (pass & 1) ? nchunk - 1 - cc : cc;
-      const int c0 = ch * kc;
-      const int rows = min(kc, n - c0);
-      if (!(pass > 0 && cc == 0)) {
-        if (pass > 0 || cc > 0) __syncthreads();
-        stage16<DT, kKcMax16>(rk, rv, Ks, Vs, c0, rows, kKeyTile, roff);
-        __syncthreads();
-      }
-      if (pass == npass - 1 && cc == nchunk - 1) last_use();
-      if (cc == 0) {  // accumulators come alive only after the first staging
+      for (int i = 0; i < 2; ++i) {
+        qb[i] = pass * kPerPass + w + i * kWaves;
+        act[i] = qb[i] < nqt;
+        const int q = (qt + qs * qb[i]) * kQBlock + r16;
+        qoff[i] = (act[i] && q < n) ? roff(q) : kOOB;
+        // B operand of S^T = K Q^T: lane (r16, g) holds Q[q][32 ks + 8 g .. + 7]
+        qf[i][0] = __builtin_bit_cast(V8, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)(qoff[i] + 16 * g), 0, 0));
+        qf[i][1] = __builtin_bit_cast(V8, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)(qoff[i] + 64 + 16 * g), 0, 0));
+        m[i] = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          m[i] = -INFINITY;
-#pragma unroll
-          for (int db = 0; db < 5; ++db) o[i][db] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-      }
-      if (act[0]) {
-        const int ntile = (rows + kKeyTile - 1) / kKeyTile;
-        for (int t = 0; t < ntile; ++t) {
-          const int k0 = t * kKeyTile;
-          const int kvalid = min(kKeyTile, rows - k0);
-          const KVFrag16<DT> f = kv_frag16<DT>(Ks, Vs, k0);
-          block_step16<DT>(f, qf[0], o[0], m[0], kvalid, c);
-          if (act[1]) block_step16<DT>(f, qf[1], o[1], m[1], kvalid, c);
-        }
+        for (int db = 0; db < 5; ++db) o[i][db] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
     }
-    // rows q >= n went to kOOB
+    // the buffer of step s + 1 was read in step s - 1: every wave is past it
+    if (s > 0) bar_lds();
+    if (s + 1 < nsteps) {
+      const int c1 = ((s + 1) % nchunk) * kChunk16;
+      unsigned char* b = kvbase + ((s + 1) & 1) * 2 * kBuf;
+      stage_chunk16(rk, rv, b, b + kBuf, c1, min(kChunk16, n - c1), roff);
+      // this wave's loads up to step s are done, step s + 1's still in flight
+      wait_vm<2 * kChunkLoads16>();
+    } else {
+      last_use();
+      wait_vm<0>();  // nothing of this wave is left in flight into LDS
+    }
+    bar_lds();  // every wave's loads of step s have landed
+    const unsigned char* Ks = kvbase + (s & 1) * 2 * kBuf;
+    const unsigned char* Vs = Ks + kBuf;
+    const int rows = min(kChunk16, n - cc * kChunk16);
+    if (act[0]) {
+      const int ntile = (rows + kKeyTile - 1) / kKeyTile;
+      for (int t = 0; t < ntile; ++t) {
+        const int k0 = t * kKeyTile;
+        const int kvalid = min(kKeyTile, rows - k0);
+        const KVFrag16<DT> f = kv_frag16<DT>(Ks, Vs, k0);
+        block_step16<DT>(f, qf[0], o[0], m[0], kvalid, c);
+        if (act[1]) block_step16<DT>(f, qf[1], o[1], m[1], kvalid, c);
+      }
+    }
+    if (cc == nchunk - 1) {
+      // rows q >= n went to kOOB
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      if (act[i]) store_block16<DT>(o[i], ro, qoff[i]);
+      for (int i = 0; i < 2; ++i)
+        if (act[i]) store_block16<DT>(o[i], ro, qoff[i]);
+    }
   }
 }
 
@@ -1032,26 +1086,25 @@ __global__ __launch_bounds__(kAttnThreads16, 3) void attend16_persistent_kernel(
   }
 }
 
-// Rows of the 16-bit staging area a launch gives whole sequences: kc when
-// the length hint is below the chunk cap; otherwise as many 16-row blocks
-// as the LDS left to each of 3 workgroups per CU holds (after the
-// compaction area and `reserved` bytes), at most kResidentMax16.  At
-// N = 197 that is 208 rows: 53248 bytes of K/V, 448 of compaction area and
-// the 16-byte item slot.
-static int resident_rows(int dtype, bool fused, int N, int kc, int reserved) {
+// Rows of the 16-bit staging area, which stages whole sequences of up to
+// that many rows: as many 16-row blocks as the LDS left to each of 3
+// workgroups per CU holds (after the compaction area and `reserved`
+// bytes), at most kResidentMax16.  At N = 197 that is 208 rows: 53248 bytes
+// of K/V, 448 of compaction area and the 16-byte item slot; at N = 1024
+// still 192, the two key buffers of the streamed form.
+static int resident_rows(int dtype, bool fused, int N, int reserved) {
   if (dtype == 0) return 0;
-  if (kc < kKcMax16) return kc;
   const long long per_wg = (long long)kLdsPerWg16 - reserved -
                            (fused ? (long long)attn_compact_bytes(N) : 0);
   int rows = (int)(per_wg / (kHeadDim * 2 * 2)) / kQBlock * kQBlock;
-  if (rows > kResidentMax16) rows = kResidentMax16;
-  return rows > kc ? rows : kc;
+  return rows > kResidentMax16 ? kResidentMax16 : rows;
 }
+static_assert((kLdsPerWg16 - kItemSlotBytes - (2 * 1024 + 16 * 12)) / (kHeadDim * 2 * 2) / kQBlock *
+                      kQBlock >= 2 * kChunk16,
+              "the streamed form's two key buffers fit the staging area at N = 1024");
 
-static int kv_rows(int dtype, int kc, int rc) { return dtype == 0 ? kc : (rc > kc ? rc : kc); }
-
-int attend_resident_rows(int dtype, bool fused, int N, int kc) {
-  return resident_rows(dtype, fused, N, kc, (fused && dtype != 0) ? kItemSlotBytes : 0);
+int attend_resident_rows(int dtype, bool fused, int N) {
+  return resident_rows(dtype, fused, N, (fused && dtype != 0) ? kItemSlotBytes : 0);
 }
 
 long long attend_grid_items(const AttnParams& p, int dtype, bool fused) {
@@ -1065,20 +1118,20 @@ long long attend_grid_items(const AttnParams& p, int dtype, bool fused) {
 // Dynamic LDS of the fused 16-bit kernels: compaction area, staging area and
 // the persistent form's item slot (reserved by both forms, so that both give
 // the same sequences the same staging).
-static size_t fused16_lds(int N, int kc, int rc) {
-  return attn_lds_bytes(1, true, N, kv_rows(1, kc, rc)) + kItemSlotBytes;
+static size_t fused16_lds(int N, int rc) {
+  return attn_lds_bytes(1, true, N, rc) + kItemSlotBytes;
 }
 
-int attend_persistent_per_cu(int N, int kc) {
-  const int rc = resident_rows(1, true, N, kc, kItemSlotBytes);
-  const int by_lds = (int)(kLdsPerCu / fused16_lds(N, kc, rc));
+int attend_persistent_per_cu(int N) {
+  const int rc = resident_rows(1, true, N, kItemSlotBytes);
+  const int by_lds = (int)(kLdsPerCu / fused16_lds(N, rc));
   return by_lds < kAttnWgPerCu16 ? by_lds : kAttnWgPerCu16;  // 3 waves per SIMD by registers
 }
 
 hipError_t launch_attend_persistent(const AttnParams& p0, int dtype, int grid, hipStream_t s) {
   AttnParams p = p0;
-  p.rc = resident_rows(dtype, true, p.N, p.kc, kItemSlotBytes);
-  const size_t lds = fused16_lds(p.N, p.kc, p.rc);
+  p.rc = resident_rows(dtype, true, p.N, kItemSlotBytes);
+  const size_t lds = fused16_lds(p.N, p.rc);
   p.item_slot = (int)(lds - kItemSlotBytes);
   if (dtype == 1)
     hipLaunchKernelGGL((attend16_persistent_kernel<1>), dim3(grid), dim3(kAttnThreads16), lds, s, p);
@@ -1111,9 +1164,8 @@ hipError_t attend_init() {
 hipError_t launch_attend(const AttnParams& p0, int dtype, bool fused, hipStream_t s) {
   AttnParams p = p0;
   const bool fused16 = fused && dtype != 0;
-  p.rc = resident_rows(dtype, fused, p.N, p.kc, fused16 ? kItemSlotBytes : 0);
-  const size_t lds = fused16 ? fused16_lds(p.N, p.kc, p.rc)
-                             : attn_lds_bytes(dtype, fused, p.N, kv_rows(dtype, p.kc, p.rc));
+  p.rc = resident_rows(dtype, fused, p.N, fused16 ? kItemSlotBytes : 0);
+  const size_t lds = fused16 ? fused16_lds(p.N, p.rc) : attn_lds_bytes(dtype, fused, p.N, p.rc);
   const int grid = (int)attend_grid_items(p, dtype, fused) +
                    ((fused && (p.cu_out || p.max_out)) ? 1 : 0);
   const dim3 blk(attn_threads(dtype));

@@ -86,14 +86,6 @@ float resolve_scale(float s, int d) {
   return s * 1.4426950408889634f;  // fold log2(e) so the kernel uses exp2
 }
 
-int pick_kc(int hint, int fallback) {
-  const int cap = rva::kKcMax16;
-  int n = hint > 0 ? hint : fallback;
-  if (n < 1) n = cap;
-  int kc = rva::round_up(n, rva::kKeyTile);
-  return kc > cap ? cap : kc;
-}
-
 // Row splits for the copy kernels: aim for enough workgroups to cover the
 // device when the batch is small.
 int copy_splits(int B, int N) {
@@ -176,7 +168,6 @@ int validate_attend(const void* q, const void* k, const void* v, const int32_t* 
   p->B = B;
   p->N = 0;
   p->H = H;
-  p->kc = pick_kc(max_seqlen, 0);
   p->nbound = max_seqlen > 0 ? max_seqlen : RVA_MAX_TOKENS;
   p->scale_log2e = resolve_scale(scale, d);
   return RVA_OK;
@@ -225,7 +216,6 @@ int validate_fused(const void* q, const void* k, const void* v, const uint8_t* m
   p->B = B;
   p->N = N;
   p->H = H;
-  p->kc = pick_kc(hint > 0 && hint < N ? hint : N, N);
   p->nbound = hint > 0 && hint < N ? hint : N;
   p->scale_log2e = resolve_scale(scale, d);
   return RVA_OK;
@@ -422,7 +412,7 @@ int plan_grid(rva::AttnParams* p, int dtype, bool fused, bool persistent, long l
     const long long t = (slots + p->H - 1) / p->H;
     p->tail_b = (int)(t < p->B ? t : p->B);
   } else if (!persistent && bh < slots) {
-    const int rc = rva::attend_resident_rows(dtype, fused, p->N, p->kc);
+    const int rc = rva::attend_resident_rows(dtype, fused, p->N);
     const bool whole = p->nbound <= rc;
     const long long per = whole ? (nqb + 3) / 4 : (nqb + 7) / 8;
     const long long fill = ((whole ? 1 : 2) * slots + bh - 1) / bh;
@@ -456,7 +446,7 @@ int enqueue_attend_persistent(const rva::AttnParams& p0, int dtype, hipStream_t 
   RVA_TRY(plan_grid(&p, dtype, true, true, &items));
   int cus = 0;
   RVA_TRY(device_cus(&cus));
-  long long grid = (long long)rva::attend_persistent_per_cu(p.N, p.kc) * cus;
+  long long grid = (long long)rva::attend_persistent_per_cu(p.N) * cus;
   if (grid > items) grid = items;
   if (grid < 1) grid = 1;
   if (items + grid >= (1ll << 31))  // excluded by check_persistent_items

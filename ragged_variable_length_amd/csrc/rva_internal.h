@@ -17,12 +17,10 @@ constexpr int kKeyTile = 32;        // keys per inner step
 constexpr int kPackThreads = 256;
 constexpr int kScanThreads = 1024;
 
-// Keys staged on chip per chunk (16-bit forms): K and V rows [kc][64] halves
-// each (16-byte pieces XOR-swizzled by row).  fp32 stages no keys.
-constexpr int kKcMax16 = 192;
 // 16-bit sequences of up to rc rows are staged whole (K and V of one head
-// in one round trip); rc is capped by the registers' query blocks (4 per
-// wave, 4 waves) and by the LDS that keeps 3 workgroups per CU.
+// in one round trip, rows of 64 halves with 16-byte pieces XOR-swizzled by
+// row); rc is capped by the registers' query blocks (4 per wave, 4 waves)
+// and by the LDS that keeps 3 workgroups per CU.  fp32 stages no keys.
 constexpr int kResidentMax16 = 256;
 constexpr int kLdsPerCu = 160 * 1024;
 constexpr int kAttnWgPerCu16 = 3;
@@ -48,11 +46,10 @@ struct AttnParams {
   int32_t* cu_out;        // fused mode: optional offsets output
   int32_t* max_out;       // fused mode: optional max kept count output
   int B, N, H;
-  int kc;                 // keys per staged chunk (multiple of kKeyTile)
   float scale_log2e;      // softmax scale * log2(e)
   int32_t* work;          // persistent form: [next item, workgroups done], zero between launches
   int heads_per_wg;       // fused 16-bit form: heads of one image a workgroup takes in turn (>= 1)
-  int rc;                 // 16-bit: longest sequence staged whole (rows, multiple of 16, >= kc); set at launch
+  int rc;                 // 16-bit: longest sequence staged whole (rows, multiple of 16, >= 192); set at launch
   int tail_b;             // fused 16-bit form: last images taken one head per workgroup (0..B)
   int item_slot;          // persistent form: byte offset of its 4-byte item slot in dynamic LDS; set at launch
   int qsplit;             // query tiles per (sequence, head): one workgroup each (>= 1; 1 with head pairs)
@@ -107,8 +104,8 @@ __host__ __device__ inline size_t attn_compact_bytes(int N) {
 
 inline int attn_threads(int dtype) { return dtype == 0 ? kAttnThreads32 : kAttnThreads16; }
 
-// kv_rows: staged key rows of the 16-bit forms (max(kc, rc)); fp32 stages
-// nothing but its combine area.
+// kv_rows: staged key rows of the 16-bit forms (rc); fp32 stages nothing but
+// its combine area.
 inline size_t attn_lds_bytes(int dtype, bool fused, int N, int kv_rows) {
   size_t kv = dtype == 0 ? (size_t)kComb32Bytes : (size_t)kv_rows * kHeadDim * 2 * 2;
   size_t head = fused ? attn_compact_bytes(N) : 0;
@@ -126,9 +123,9 @@ hipError_t launch_attend(const AttnParams& p, int dtype, bool fused, hipStream_t
 // Fused 16-bit path as a persistent grid of `grid` workgroups pulling
 // (image, head) items from p.work.
 hipError_t launch_attend_persistent(const AttnParams& p, int dtype, int grid, hipStream_t s);
-int attend_persistent_per_cu(int N, int kc);  // resident workgroups per CU
+int attend_persistent_per_cu(int N);  // resident workgroups per CU
 // Longest sequence a 16-bit launch stages whole (rows), as launch_attend sets it.
-int attend_resident_rows(int dtype, bool fused, int N, int kc);
+int attend_resident_rows(int dtype, bool fused, int N);
 // Grid positions of a launch's work items (without the offsets workgroup).
 long long attend_grid_items(const AttnParams& p, int dtype, bool fused);
 hipError_t launch_empty(hipStream_t s);
