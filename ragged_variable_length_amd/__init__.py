@@ -91,6 +91,10 @@ def lib() -> ctypes.CDLL:
     L.rva_plan_destroy.argtypes = [P]
     L.rva_empty.argtypes = [I, P]
     L.rva_set_query_split.argtypes = [I]
+    LL = ctypes.c_longlong
+    L.rva_probe_copy.argtypes = [P, P, LL, I, P]
+    L.rva_probe_read.argtypes = [P, P, LL, I, P]
+    L.rva_probe_mfma.argtypes = [I, P, I, P, ctypes.POINTER(LL)]
     L.rva_threshold_l2_mask.argtypes = [P, I, I, I, I, ctypes.c_double, P, P]
     L.rva_qkv_projection.argtypes = [P, P, P, I, I, I, P, P, I, P, P, P, P]
     L.rva_out_projection.argtypes = [P, P, P, P, I, I, I, P, P, P, I, P, P]
@@ -103,7 +107,8 @@ def lib() -> ctypes.CDLL:
                  "rva_plan_launch", "rva_plan_destroy", "rva_empty", "rva_version",
                  "rva_threshold_l2_mask", "rva_qkv_projection", "rva_out_projection",
                  "rva_layers_plan_create", "rva_fused_persistent",
-                 "rva_fused_persistent_noalloc", "rva_set_query_split"):
+                 "rva_fused_persistent_noalloc", "rva_set_query_split", "rva_probe_copy",
+                 "rva_probe_read", "rva_probe_mfma"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -527,6 +532,35 @@ def set_query_split(split: int):
     """Query tiles per (sequence, head) on every later attention launch of
     this process (0: each launch chooses; results never depend on it)."""
     _check(lib().rva_set_query_split(int(split)), "rva_set_query_split")
+
+
+def probe_copy(src, dst, grid: int, stream=None):
+    """Ceiling probe: copy src into dst (same byte size, a multiple of 16)."""
+    _dev(src, "src")
+    _dev(dst, "dst", numel=0)
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("src and dst must have the same size in bytes")
+    _check(lib().rva_probe_copy(_ptr(src), _ptr(dst), nbytes, int(grid), _stream(stream)),
+           "rva_probe_copy")
+
+
+def probe_read(src, sink, grid: int, stream=None):
+    """Ceiling probe: read every byte of src; sink: int32 [grid * 256]."""
+    _dev(src, "src")
+    _dev(sink, "sink", dtype=torch.int32, numel=int(grid) * 256)
+    _check(lib().rva_probe_read(_ptr(src), _ptr(sink), src.numel() * src.element_size(), int(grid),
+                                _stream(stream)), "rva_probe_read")
+
+
+def probe_mfma(iters: int, out, grid: int, stream=None) -> int:
+    """Ceiling probe: fp16 matrix-core products; out: float32 [grid * 256].
+    Returns the FLOPs of the launch."""
+    _dev(out, "out", dtype=torch.float32, numel=int(grid) * 256)
+    fl = ctypes.c_longlong(0)
+    _check(lib().rva_probe_mfma(int(iters), _ptr(out), int(grid), _stream(stream),
+                                ctypes.byref(fl)), "rva_probe_mfma")
+    return fl.value
 
 
 def empty(count: int = 1, stream=None):

@@ -4,7 +4,8 @@ import subprocess
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SOURCES = ["csrc/pack.hip", "csrc/attend.hip", "csrc/threshold.hip", "csrc/linear.hip", "csrc/rva_host.hip"]
+SOURCES = ["csrc/pack.hip", "csrc/attend.hip", "csrc/threshold.hip", "csrc/linear.hip", "csrc/probe.hip",
+           "csrc/rva_host.hip"]
 LIB = os.path.join(PKG, "librva.so")
 
 

@@ -16,6 +16,7 @@
 #include <vector>
 
 #include "rva.h"
+#include "rva_probe.h"
 #include "rva_internal.h"
 
 namespace {
@@ -684,6 +685,38 @@ int rva_fused_persistent_noalloc(const void* q_pad, const void* k_pad, const voi
 int rva_set_query_split(int split) {
   if (split < 0) return fail(RVA_ERR_INVALID, "split must be >= 0 (got %d)", split);
   g_query_split.store(split, std::memory_order_relaxed);
+  return RVA_OK;
+}
+
+int rva_probe_copy(const void* src, void* dst, long long bytes, int grid, void* stream) {
+  RVA_TRY(check_data(src, "src", true));
+  RVA_TRY(check_data(dst, "dst", true));
+  if (bytes <= 0 || bytes % 16) return fail(RVA_ERR_INVALID, "bytes must be a positive multiple of 16");
+  if (grid < 1) return fail(RVA_ERR_INVALID, "grid must be >= 1");
+  const char* s0 = static_cast<const char*>(src);
+  const char* d0 = static_cast<const char*>(dst);
+  if (s0 < d0 + bytes && d0 < s0 + bytes) return fail(RVA_ERR_INVALID, "src and dst overlap");
+  hipError_t e = rva::launch_probe_copy(src, dst, bytes / 16, grid, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "copy probe launch");
+  return RVA_OK;
+}
+
+int rva_probe_read(const void* src, uint32_t* sink, long long bytes, int grid, void* stream) {
+  RVA_TRY(check_data(src, "src", true));
+  RVA_TRY(check_i32(sink, "sink", true));
+  if (bytes <= 0 || bytes % 16) return fail(RVA_ERR_INVALID, "bytes must be a positive multiple of 16");
+  if (grid < 1) return fail(RVA_ERR_INVALID, "grid must be >= 1");
+  hipError_t e = rva::launch_probe_read(src, sink, bytes / 16, grid, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "read probe launch");
+  return RVA_OK;
+}
+
+int rva_probe_mfma(int iters, float* out, int grid, void* stream, long long* flops) {
+  RVA_TRY(check_i32(out, "out", true));
+  if (iters < 1 || grid < 1) return fail(RVA_ERR_INVALID, "iters and grid must be >= 1");
+  if (flops) *flops = rva::probe_mfma_flops(iters, grid);
+  hipError_t e = rva::launch_probe_mfma(iters, out, grid, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "matrix-core probe launch");
   return RVA_OK;
 }
 

@@ -135,5 +135,11 @@ hipError_t threshold_init();  // raises the dynamic-LDS limit of the keep-mask k
 hipError_t launch_linear(const LinearParams& p, int dtype, hipStream_t s);
 int linear_tile_rows();
 int linear_tile_cols();
+// Ceiling probes (probe.hip).
+hipError_t launch_probe_copy(const void* src, void* dst, long long pieces, int grid, hipStream_t s);
+hipError_t launch_probe_read(const void* src, uint32_t* sink, long long pieces, int grid,
+                             hipStream_t s);
+hipError_t launch_probe_mfma(int iters, float* out, int grid, hipStream_t s);
+long long probe_mfma_flops(int iters, int grid);
 
 }  // namespace rva

@@ -8,11 +8,11 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "rva.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("rva.h", "rva_probe.h")]
 
 
 def _declared():
-    src = open(HEADER).read()
+    src = "\n".join(open(h).read() for h in HEADERS)
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(rva_[a-z0-9_]+)\s*\(",
                        src, flags=re.M)
@@ -200,3 +200,16 @@ def test_persistent_item_limit(L):
     st = L.rva_fused_persistent_noalloc(FAKE, FAKE, FAKE, None, 4, 8, 2, 64, 0, f, 1, FAKE,
                                         None, None, None)
     assert st == -1 and b"mask" in L.rva_last_error()
+
+
+def test_probe_validation(L):
+    """The ceiling probes reject bad sizes and overlapping buffers before any
+    HIP call."""
+    LL = ctypes.c_longlong
+    assert L.rva_probe_copy(FAKE, MIS, LL(1024), 4, None) == -1 and b"aligned" in L.rva_last_error()
+    assert L.rva_probe_copy(FAKE, ctypes.c_void_p(0x7F0000000100), LL(1024), 4, None) == -1
+    assert b"overlap" in L.rva_last_error()
+    assert L.rva_probe_copy(FAKE, ctypes.c_void_p(0x7F0000100000), LL(24), 4, None) == -1
+    assert L.rva_probe_read(FAKE, FAKE, LL(0), 4, None) == -1
+    assert L.rva_probe_read(FAKE, FAKE, LL(1024), 0, None) == -1
+    assert L.rva_probe_mfma(0, FAKE, 4, None, None) == -1
