@@ -80,6 +80,13 @@ struct Half16<2> {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Cache-policy operand of the 16-bit path's global accesses (gfx950 buffer
+// instructions: bit 1 is the non-temporal hint).  Q/K/V rows and output
+// rows are each touched once per launch.
+constexpr int kLoadAux = 0;   // Q loads and K/V staging loads
+constexpr int kStoreAux = 0;  // output rows
+constexpr bool kZeroNT = false;  // zero rows of pruned tokens as non-temporal stores
+
 // Reductions over the four lanes l, l^16, l^32, l^48 that share a query:
 // a lane-swap exchanges 16-lane (resp. 32-lane) rows between two copies of
 // the value, after which the elementwise max/sum of the copies is the
@@ -376,8 +383,79 @@ __device__ __forceinline__ void store_block16(const f32x4 (&o)[5], Rsrc ro, uint
 #pragma unroll
     for (int j = 0; j < 4; ++j) out[j] = (T)(o[db][j] * inv);
     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, out), ro,
-                                          (int)(qoff + db * 32 + 8 * g), 0, 0);
+                                          (int)(qoff + db * 32 + 8 * g), 0, kStoreAux);
   }
+}
+
+// One 16-query block against one 32-key tile of the streamed form, with the
+// fixed reference max: `first` (the pass's first tile) sets m to the tile's
+// row max, later tiles use m as it is.
+template <int DT>
+__device__ __forceinline__ void stream_step16(const KVFrag16<DT>& f,
+                                              const typename Half16<DT>::V8 (&qf)[2],
+                                              f32x4 (&o)[5], float& m, int kvalid, float c,
+                                              bool first) {
+  f32x4 s0, s1;
+  scores16<DT>(f.kf, qf, s0, s1);
+  mask_keys(s0, s1, kvalid);
+  if (first) {
+    m = quad_max(max8(s0, s1)) * c;
+    fixed_step16<DT, true>(f.vf, s0, s1, o, m, c);
+  } else {
+    fixed_step16<DT, false>(f.vf, s0, s1, o, m, c);
+  }
+}
+
+// Exact fallback of the streamed form for a query block whose probabilities
+// against the fixed reference max left range (rare: some later key scores
+// far above every key of the block's first tile): the block computed again
+// from scratch with a running max and rescaling, reading K and V straight
+// from memory, so it needs nothing from the workgroup's other waves.  Rows
+// at or past n read as zeros; qf is the block's Q operand, qoff the byte
+// offset of its output row (kOOB past n).
+template <int DT, typename RowOff>
+__device__ __forceinline__ void block_exact16(Rsrc rk, Rsrc rv, Rsrc ro, int n,
+                                                        RowOff roff, float c,
+                                                        typename Half16<DT>::V8 q0,
+                                                        typename Half16<DT>::V8 q1,
+                                                        uint32_t qoff) {
+  typedef Half16<DT> Tr;
+  typedef typename Tr::V8 V8;
+  typedef typename Tr::T T;
+  const int lane = lane_id(), g = lane >> 4, r16 = lane & 15;
+  const V8 qf[2] = {q0, q1};
+  f32x4 o[5];
+#pragma unroll
+  for (int db = 0; db < 5; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY;
+  for (int k0 = 0; k0 < n; k0 += kKeyTile) {
+    V8 kf[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int row = k0 + kb * 16 + r16;
+      const uint32_t base = row < n ? roff(row) : kOOB;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        kf[kb][ks] = __builtin_bit_cast(
+            V8, __builtin_amdgcn_raw_buffer_load_b128(rk, (int)(base + 64 * ks + 16 * g), 0, 0));
+    }
+    // V^T operand: lane (r16, g) element j is V[key][16 db + r16] with key
+    // 4 g + j (j < 4) or 16 + 4 g + j - 4 (j >= 4) of the tile
+    V8 vf[4];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int key = k0 + (j < 4 ? 4 * g + j : 16 + 4 * g + j - 4);
+      const uint32_t base = key < n ? roff(key) : kOOB;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+        vf[db][j] = __builtin_bit_cast(
+            T, __builtin_amdgcn_raw_buffer_load_b16(rv, (int)(base + 2 * (16 * db + r16)), 0, 0));
+    }
+    f32x4 s0, s1;
+    scores16<DT>(kf, qf, s0, s1);
+    prob_step16<DT>(vf, s0, s1, o, m, min(kKeyTile, n - k0), c);
+  }
+  store_block16<DT>(o, ro, qoff);
 }
 
 // Global accesses of the 16-bit path go through raw buffer descriptors
@@ -416,9 +494,9 @@ __device__ __forceinline__ void stage16(Rsrc rk, Rsrc rv, unsigned char* Ks, uns
     const int r0 = 8 * (w + kWaves * i);
     if (r0 >= rpad) break;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(Ks + r0 * 128),
-                                             16, off[i], 0, 0, 0);
+                                             16, off[i], 0, 0, kLoadAux);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(Vs + r0 * 128),
-                                             16, off[i], 0, 0, 0);
+                                             16, off[i], 0, 0, kLoadAux);
   }
 }
 
@@ -467,9 +545,9 @@ __device__ __forceinline__ void stage_chunk16(Rsrc rk, Rsrc rv, unsigned char* K
   for (int i = 0; i < kChunkLoads16; ++i) {
     const int r0 = 8 * (w + kWaves * i);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(Ks + r0 * 128),
-                                             16, off[i], 0, 0, 0);
+                                             16, off[i], 0, 0, kLoadAux);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(Vs + r0 * 128),
-                                             16, off[i], 0, 0, 0);
+                                             16, off[i], 0, 0, kLoadAux);
   }
 }
 
@@ -505,6 +583,7 @@ __device__ __forceinline__ void attend_seq16(const AttnParams& p, int n, unsigne
   V8 qf[2][2];
   f32x4 o[2][5];
   float m[2];
+  uint32_t redo = 0;  // blocks to compute again exactly: bit 2 pass + i (at most 8 passes)
   for (int s = 0; s < nsteps; ++s) {
     const int pass = s / nchunk, cc = s - pass * nchunk;
     if (cc == 0) {
@@ -515,8 +594,8 @@ __device__ __forceinline__ void attend_seq16(const AttnParams& p, int n, unsigne
         const int q = (qt + qs * qb[i]) * kQBlock + r16;
         qoff[i] = (act[i] && q < n) ? roff(q) : kOOB;
         // B operand of S^T = K Q^T: lane (r16, g) holds Q[q][32 ks + 8 g .. + 7]
-        qf[i][0] = __builtin_bit_cast(V8, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)(qoff[i] + 16 * g), 0, 0));
-        qf[i][1] = __builtin_bit_cast(V8, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)(qoff[i] + 64 + 16 * g), 0, 0));
+        qf[i][0] = __builtin_bit_cast(V8, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)(qoff[i] + 16 * g), 0, kLoadAux));
+        qf[i][1] = __builtin_bit_cast(V8, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)(qoff[i] + 64 + 16 * g), 0, kLoadAux));
         m[i] = -INFINITY;
 #pragma unroll
         for (int db = 0; db < 5; ++db) o[i][db] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -539,21 +618,45 @@ __device__ __forceinline__ void attend_seq16(const AttnParams& p, int n, unsigne
     const unsigned char* Vs = Ks + kBuf;
     const int rows = min(kChunk16, n - cc * kChunk16);
     if (act[0]) {
+      // softmax against a fixed reference max per query block: the pass's
+      // first tile sets it to that tile's row max, later tiles use it as it
+      // is, with no running max and no rescale (as the whole-sequence form)
       const int ntile = (rows + kKeyTile - 1) / kKeyTile;
       for (int t = 0; t < ntile; ++t) {
         const int k0 = t * kKeyTile;
         const int kvalid = min(kKeyTile, rows - k0);
         const KVFrag16<DT> f = kv_frag16<DT>(Ks, Vs, k0);
-        block_step16<DT>(f, qf[0], o[0], m[0], kvalid, c);
-        if (act[1]) block_step16<DT>(f, qf[1], o[1], m[1], kvalid, c);
+        // two calls, not an unrolled loop over the blocks with an early
+        // exit: written that way, the second block's reference max came out
+        // wrong with this toolchain (every pass, both forms, GPU tests)
+        const bool first = cc == 0 && t == 0;
+        stream_step16<DT>(f, qf[0], o[0], m[0], kvalid, c, first);
+        if (act[1]) stream_step16<DT>(f, qf[1], o[1], m[1], kvalid, c, first);
       }
     }
     if (cc == nchunk - 1) {
-      // rows q >= n went to kOOB
+      // rows q >= n went to kOOB; a block whose row sums left the fixed
+      // reference's range is computed again exactly once the passes are
+      // done (its bit 2 pass + i), when the passes' registers are free
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        if (act[i]) store_block16<DT>(o[i], ro, qoff[i]);
+      for (int i = 0; i < 2; ++i) {
+        if (!act[i]) continue;
+        if (__any(!(o[i][4][0] <= kRefSumLimit)))
+          redo |= 1u << (2 * pass + i);
+        else
+          store_block16<DT>(o[i], ro, qoff[i]);
+      }
     }
+  }
+  while (redo) {
+    const int bit = __builtin_ctz(redo);
+    redo &= redo - 1;
+    const int qbl = (bit >> 1) * kPerPass + w + (bit & 1) * kWaves;
+    const int q = (qt + qs * qbl) * kQBlock + r16;
+    const uint32_t off = q < n ? roff(q) : kOOB;
+    const V8 q0 = __builtin_bit_cast(V8, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)(off + 16 * g), 0, 0));
+    const V8 q1 = __builtin_bit_cast(V8, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)(off + 64 + 16 * g), 0, 0));
+    block_exact16<DT>(rk, rv, ro, n, roff, c, q0, q1, off);
   }
 }
 
@@ -607,8 +710,8 @@ __device__ __forceinline__ void attend_resident16(int n, int nh, float c, unsign
   }
   auto load_q = [&](uint32_t off, V8 (&qs)[2]) {
     // B operand of S^T = K Q^T: lane (r16, g) holds Q[q][32 ks + 8 g .. + 7]
-    qs[0] = __builtin_bit_cast(V8, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)(off + 16 * g), 0, 0));
-    qs[1] = __builtin_bit_cast(V8, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)(off + 64 + 16 * g), 0, 0));
+    qs[0] = __builtin_bit_cast(V8, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)(off + 16 * g), 0, kLoadAux));
+    qs[1] = __builtin_bit_cast(V8, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)(off + 64 + 16 * g), 0, kLoadAux));
   };
   V8 qf[kQSlots][2];
 #pragma unroll
@@ -862,7 +965,13 @@ __device__ __forceinline__ void zero_pruned(char* o, const uint64_t* ballots, in
   for (int e = threadIdx.x + part * NT; e < total; e += parts * NT) {
     const int j = e / PIECES, pc = e - j * PIECES;
     const bool kept = (ballots[j >> 6] >> (j & 63)) & 1ull;
-    if (!kept) *reinterpret_cast<u32x4*>(o + (uint32_t)j * rs + pc * 16) = u32x4{0u, 0u, 0u, 0u};
+    if (!kept) {
+      u32x4* dst = reinterpret_cast<u32x4*>(o + (uint32_t)j * rs + pc * 16);
+      if constexpr (kZeroNT)
+        __builtin_nontemporal_store(u32x4{0u, 0u, 0u, 0u}, dst);
+      else
+        *dst = u32x4{0u, 0u, 0u, 0u};
+    }
   }
 }
 

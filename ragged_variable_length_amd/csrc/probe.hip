@@ -3,20 +3,27 @@
 // vendor library's, so that a kernel's fraction of "achievable" has a
 // denominator of known construction.  Not part of the attention path.
 //
-//  - copy: every thread moves 16-byte pieces, kCopyUnroll loads in flight
-//    before their stores, over a grid-stride loop (bytes read + written);
-//  - read: the same loads, folded into a per-thread XOR and one 4-byte store
-//    per thread to a sink (bytes read; the sink's writes are negligible);
+//  - copy: every thread moves 16-byte pieces over a grid-stride loop with
+//    non-temporal loads and stores (bytes read + written);
+//  - read: non-temporal 16-byte loads, kReadUnroll in flight per thread,
+//    folded into a per-thread XOR and one 4-byte store per thread to a sink
+//    (bytes read; the sink's writes are negligible);
 //  - mfma: independent 16x16x32 fp16 matrix-core products on register
 //    operands, kMfmaChains accumulators per wave so consecutive products do
 //    not wait on each other; one store per lane at the end.
+// Measured on MI355X over 1 GiB, the best of the shapes tried: the copy at
+// one piece in flight and 4 workgroups of 256 threads per CU (about 5.97
+// TB/s read + written), the read at four in flight and 2 workgroups per CU
+// (about 7.07 TB/s); plain loads and stores, and deeper unrolls, stayed at
+// 4.3-5.5 TB/s.  The matrix cores reach about 2.19 PFLOP/s with 8 waves
+// per SIMD.
 #include "rva_device.h"
 #include "rva_internal.h"
 
 namespace rva {
 
 constexpr int kProbeThreads = 256;
-constexpr int kCopyUnroll = 4;
+constexpr int kReadUnroll = 4;
 constexpr int kMfmaChains = 8;
 
 typedef _Float16 f16x8p __attribute__((ext_vector_type(8)));
@@ -26,15 +33,8 @@ __global__ __launch_bounds__(kProbeThreads) void probe_copy_kernel(const u32x4* 
                                                                    u32x4* __restrict__ dst,
                                                                    long long n) {
   const long long stride = (long long)gridDim.x * kProbeThreads;
-  long long i = (long long)blockIdx.x * kProbeThreads + threadIdx.x;
-  for (; i + (kCopyUnroll - 1) * stride < n; i += kCopyUnroll * stride) {
-    u32x4 v[kCopyUnroll];
-#pragma unroll
-    for (int u = 0; u < kCopyUnroll; ++u) v[u] = src[i + u * stride];
-#pragma unroll
-    for (int u = 0; u < kCopyUnroll; ++u) dst[i + u * stride] = v[u];
-  }
-  for (; i < n; i += stride) dst[i] = src[i];
+  for (long long i = (long long)blockIdx.x * kProbeThreads + threadIdx.x; i < n; i += stride)
+    __builtin_nontemporal_store(__builtin_nontemporal_load(&src[i]), &dst[i]);
 }
 
 __global__ __launch_bounds__(kProbeThreads) void probe_read_kernel(const u32x4* __restrict__ src,
@@ -43,14 +43,17 @@ __global__ __launch_bounds__(kProbeThreads) void probe_read_kernel(const u32x4* 
   const long long stride = (long long)gridDim.x * kProbeThreads;
   long long i = (long long)blockIdx.x * kProbeThreads + threadIdx.x;
   uint32_t acc = 0;
-  for (; i + (kCopyUnroll - 1) * stride < n; i += kCopyUnroll * stride) {
-    u32x4 v[kCopyUnroll];
+  for (; i + (kReadUnroll - 1) * stride < n; i += kReadUnroll * stride) {
+    u32x4 v[kReadUnroll];
 #pragma unroll
-    for (int u = 0; u < kCopyUnroll; ++u) v[u] = src[i + u * stride];
+    for (int u = 0; u < kReadUnroll; ++u) v[u] = __builtin_nontemporal_load(&src[i + u * stride]);
 #pragma unroll
-    for (int u = 0; u < kCopyUnroll; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+    for (int u = 0; u < kReadUnroll; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
   }
-  for (; i < n; i += stride) acc ^= src[i][0] ^ src[i][1] ^ src[i][2] ^ src[i][3];
+  for (; i < n; i += stride) {
+    const u32x4 v = __builtin_nontemporal_load(&src[i]);
+    acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+  }
   sink[(long long)blockIdx.x * kProbeThreads + threadIdx.x] = acc;
 }
 

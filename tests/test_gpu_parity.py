@@ -300,18 +300,25 @@ def test_deterministic(device):
     assert np.array_equal(bits(a), bits(b))
 
 
+LATE_KEY_SHAPES = {"resident": (197, [197, 150, 100, 70, 40, 33]),
+                   "streamed": (600, [577, 300, 209])}
+
+
+@pytest.mark.parametrize("shape", sorted(LATE_KEY_SHAPES))
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-def test_late_dominant_key(device, dtype):
+def test_late_dominant_key(device, dtype, shape):
     """Scores in a later key tile far above every score of the first tile
-    (queries aligned with one late key and scaled up): the whole-sequence
-    form's reference max from the first tile is exceeded by much more than
-    its headroom, so those query blocks are computed again against their
-    exact max.  Fused and packed forms against the oracle."""
+    (queries aligned with one late key and scaled up): the fixed reference
+    max from the first tile is exceeded by much more than its headroom, so
+    those query blocks are computed again exactly (against their exact max
+    in the whole-sequence form; with a running max from memory in the
+    streamed form, sequences longer than the staging).  Fused and packed
+    forms against the oracle."""
     rva = _rva()
-    B, N, H = 6, 197, 2
-    counts = [197, 150, 100, 70, 40, 33]
-    w = W.random_workload(41 if dtype == "f16" else 42, B=B, N=N, H=H, dtype=dtype,
-                          counts=counts, name=f"late_key_{dtype}")
+    N, counts = LATE_KEY_SHAPES[shape]
+    B, H = len(counts), 2
+    w = W.random_workload((41 if dtype == "f16" else 42) + (10 if shape == "streamed" else 0), B=B,
+                          N=N, H=H, dtype=dtype, counts=counts, name=f"late_key_{dtype}_{shape}")
     q = oracle.decode(w.q, dtype)
     k = oracle.decode(w.k, dtype)
     for b in range(B):
@@ -330,7 +337,7 @@ def test_late_dominant_key(device, dtype):
     ref, cu_ref, _, _ = oracle.pack_attend_unpack(w.q, w.k, w.v, w.mask, w.dtype)
     assert np.isfinite(f64(o)).all()
     err = max_err(f64(o), ref)
-    _say(f"[late key] {dtype} max abs err {err:.3e}")
+    _say(f"[late key] {dtype} {shape} max abs err {err:.3e}")
     assert err <= TOL[w.dtype]
     T = int(cu_ref[-1])
     ref_pk = ref.reshape(-1, H, w.d)[oracle.kept_index(w.mask)]
