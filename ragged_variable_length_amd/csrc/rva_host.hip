@@ -389,8 +389,9 @@ std::atomic<int> g_query_split{0};
 //  - Launches with fewer (sequence, head) items than resident slots split
 //    each item into S query tiles, one workgroup each: as many tiles as
 //    leave every wave at most one 16-query block (one pass of two blocks in
-//    the chunked form), but no more than the slots need.  Otherwise most
-//    compute units would sit idle while a few run whole sequences.
+//    the streamed form), but no more than one slot-fill of workgroups needs
+//    (four for the streamed form).  Otherwise most compute units would sit
+//    idle while a few run whole sequences.
 //  - fp32 takes one workgroup per 16-query block (its waves split the keys).
 // The persistent form (`persistent`) never splits.  `items` (if not NULL)
 // receives the grid positions of the work items.
@@ -416,7 +417,10 @@ int plan_grid(rva::AttnParams* p, int dtype, bool fused, bool persistent, long l
     const int rc = rva::attend_resident_rows(dtype, fused, p->N);
     const bool whole = p->nbound <= rc;
     const long long per = whole ? (nqb + 3) / 4 : (nqb + 7) / 8;
-    const long long fill = ((whole ? 1 : 2) * slots + bh - 1) / bh;
+    // streamed sequences: one pass over the keys per workgroup is worth up to
+    // four slot-fills of workgroups (a second pass re-streams every key for
+    // the few blocks left over)
+    const long long fill = ((whole ? 1 : 4) * slots + bh - 1) / bh;
     const long long q = per < fill ? per : fill;
     p->qsplit = q > 1 ? (int)q : 1;
   }
