@@ -181,13 +181,18 @@ def make_plans(ctx, w, tensors, staged=True):
     return plans
 
 
-def fused_call(ctx, tensors, hint):
-    """The direct single-launch path (one kernel, no graph)."""
+def fused_call(ctx, tensors, hint, form="fused"):
+    """The direct single-launch path (one kernel, no graph); form
+    "persistent" launches the persistent grid instead (profiling only)."""
     t, rva = ctx.torch, ctx.rva
     q, k, v, mask = tensors
     out = t.empty_like(q)
     cu = t.empty(q.shape[0] + 1, dtype=t.int32, device=ctx.dev)
     mx = t.empty(1, dtype=t.int32, device=ctx.dev)
+    if form == "persistent":
+        work = t.zeros(2, dtype=t.int32, device=ctx.dev)
+        return lambda: rva.fused_persistent(q, k, v, mask, work, out=out, cu_seqlens=cu,
+                                            max_seqlen=mx, max_seqlen_hint=hint)
     return lambda: rva.fused(q, k, v, mask, out=out, cu_seqlens=cu, max_seqlen=mx,
                              max_seqlen_hint=hint)
 
@@ -395,18 +400,18 @@ def measure_ceilings(ctx):
     a = t.ones(nbytes // 4, dtype=t.float32, device=ctx.dev)
     b = t.empty_like(a)
     cus = t.cuda.get_device_properties(ctx.dev).multi_processor_count
-    grid = 8 * cus
-    sink = t.empty(grid * 256, dtype=t.int32, device=ctx.dev)
+    sink = t.empty(2 * cus * 256, dtype=t.int32, device=ctx.dev)
 
     def timed(fn, reps):
-        for _ in range(3):
+        for _ in range(5):
             fn()
         return ctx.events_time(fn, reps)
-    copy_us = timed(lambda: rva.probe_copy(a, b, grid), 10)
-    read_us = timed(lambda: rva.probe_read(a, sink, grid), 10)
-    out = t.empty(4 * cus * 256, dtype=t.float32, device=ctx.dev)
-    mflops = rva.probe_mfma(4096, out, 4 * cus)
-    mfma_us = timed(lambda: rva.probe_mfma(4096, out, 4 * cus), 5)
+    # launch shapes: the best of a sweep on MI355X (csrc/probe.hip)
+    copy_us = timed(lambda: rva.probe_copy(a, b, 4 * cus), 30)
+    read_us = timed(lambda: rva.probe_read(a, sink, 2 * cus), 30)
+    out = t.empty(8 * cus * 256, dtype=t.float32, device=ctx.dev)
+    mflops = rva.probe_mfma(2048, out, 8 * cus)
+    mfma_us = timed(lambda: rva.probe_mfma(2048, out, 8 * cus), 10)
     del a, b, sink, out
     m = t.randn(8192, 8192, dtype=t.float16, device=ctx.dev)
     mm_us = timed(lambda: t.matmul(m, m), 5)
@@ -414,8 +419,9 @@ def measure_ceilings(ctx):
     return {"copy_GBps": round(2 * nbytes / (copy_us * 1e-6) / 1e9, 1),
             "read_GBps": round(nbytes / (read_us * 1e-6) / 1e9, 1),
             "mfma_fp16_TFLOPs": round(mflops / (mfma_us * 1e-6) / 1e12, 1),
-            "kernels": "csrc/probe.hip (copy, read: 16-byte pieces, 4 in flight per thread, "
-                       f"{grid} workgroups; matrix cores: 8 independent 16x16x32 fp16 chains per wave)",
+            "kernels": "csrc/probe.hip (non-temporal 16-byte copy at 4 workgroups per CU and read "
+                       "at 2 per CU, 4 loads in flight per thread; matrix cores: 8 independent "
+                       "16x16x32 fp16 chains per wave, 8 waves per SIMD)",
             "vendor_fp16_matmul_8192_TFLOPs": round(2 * 8192 ** 3 / (mm_us * 1e-6) / 1e12, 1)}
 
 
@@ -559,11 +565,12 @@ PROFILE_WORKLOADS = {
 _ROCPROF = "cd /tmp && export TMPDIR=/tmp && "
 
 
-def profile_commands(name):
+def profile_commands(name, form="fused"):
     """The rocprofv3 commands (from the repository root R, after building)
-    whose output the summaries of workload `name` come from."""
-    tgt = f"-- python3 $R/bench.py --profile {name}"
-    d = f"$R/gpurun_out/prof_{name}"
+    whose output the summaries of workload `name` (launch form `form`) come
+    from."""
+    tgt = f"-- python3 $R/bench.py --profile {name}" + (f" --form {form}" if form != "fused" else "")
+    d = f"$R/gpurun_out/prof_{name}" + (f"_{form}" if form != "fused" else "")
     return {
         "trace": _ROCPROF + f"rocprofv3 --kernel-trace --stats --output-format csv -d {d}_trace "
                  f"-o fused {tgt}   # R = repository root",
@@ -722,16 +729,18 @@ def summarize_all(trace_dir, cmds, top=30):
     print("\n".join(lines))
 
 
-def summarize_util(util_dir, name="mixed_b1024"):
+def summarize_util(util_dir, name="mixed_b1024", form="fused"):
     """Matrix-core and VALU utilisation of the fused kernel from the "util"
     counter run: MfmaUtil = MFMA busy cycles / (GUI-active cycles x SIMDs),
     VALUBusy = VALU-active cycles / (GUI-active cycles x CUs), with the
     GUI-active count of the busiest XCD; instruction counts per launch."""
     import glob
     import workloads as W
-    cmds = profile_commands(name)
+    cmds = profile_commands(name, form)
     w = PROFILE_WORKLOADS[name](W)
     kern = profile_kernel(w)
+    if form == "persistent":
+        kern = kern.replace("attend16_kernel<", "attend16_persistent_kernel<").replace(", true>", ">")
     rows = _read_csv(glob.glob(os.path.join(util_dir, "*counter_collection.csv"))[0])
     per = {}
     durs = {}
@@ -769,7 +778,8 @@ def summarize_util(util_dir, name="mixed_b1024"):
               f"| transcendental (exp2, rcp) per MFMA | {m['SQ_INSTS_VALU_TRANS_F32'] / m['SQ_INSTS_MFMA']:.2f} |",
               f"| LDS instructions per MFMA | {m['SQ_INSTS_LDS'] / m['SQ_INSTS_MFMA']:.2f} |", "",
               f"Kernel source hash (attend.hip, rva_device.h, rva_internal.h): `{kernel_source_hash()}`"]
-    with open(os.path.join(ROOT, "profiles", f"fused_{name}_utilisation.md"), "w") as f:
+    suffix = "_persistent" if form == "persistent" else ""
+    with open(os.path.join(ROOT, "profiles", f"fused_{name}{suffix}_utilisation.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
@@ -790,6 +800,8 @@ def main():
                     help="write the profiles/ summaries from rocprofv3 output of --profile runs")
     ap.add_argument("--name", default="mixed_b1024", choices=sorted(PROFILE_WORKLOADS),
                     help="workload of --summarize / --summarize-util")
+    ap.add_argument("--form", default="fused", choices=["fused", "persistent"],
+                    help="launch form of a --profile run, and of --summarize-util")
     ap.add_argument("--summarize-all", metavar="TRACE_DIR",
                     help="write the profiles/ summary of every kernel from a traced full bench run")
     ap.add_argument("--summarize-util", metavar="UTIL_DIR",
@@ -803,7 +815,7 @@ def main():
         summarize_all(args.summarize_all, PROFILE_COMMANDS)
         return
     if args.summarize_util:
-        summarize_util(args.summarize_util, args.name)
+        summarize_util(args.summarize_util, args.name, args.form)
         return
     if args.summarize:
         summarize_profiles(*args.summarize, args.name)
@@ -827,12 +839,12 @@ def main():
     dev = torch.device("cuda:0")
     ctx = Ctx(torch, rva, dev)
 
-    log("generating the mixed batch ...")
+    log(f"generating the {args.profile or 'mixed_b1024'} workload ...")
     w = PROFILE_WORKLOADS[args.profile](W) if args.profile else W.mixed_peak()
     stats = workload_stats(w)
     tensors = upload(ctx, w)
     hint = int(w.counts.max())
-    step = fused_call(ctx, tensors, hint)
+    step = fused_call(ctx, tensors, hint, args.form if args.profile else "fused")
 
     if args.profile:
         # rocprofv3 target: first the library's read and copy probes over 256
@@ -842,11 +854,11 @@ def main():
         a = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
         b = torch.empty_like(a)
         cus = torch.cuda.get_device_properties(dev).multi_processor_count
-        sink = torch.empty(8 * cus * 256, dtype=torch.int32, device=dev)
+        sink = torch.empty(2 * cus * 256, dtype=torch.int32, device=dev)
         for _ in range(3):
-            rva.probe_read(a, sink, 8 * cus)
+            rva.probe_read(a, sink, 2 * cus)
         for _ in range(3):
-            rva.probe_copy(a, b, 8 * cus)
+            rva.probe_copy(a, b, 4 * cus)
         torch.cuda.synchronize()
         del a, b, sink
         args.quick = args.no_cpu = True
