@@ -57,7 +57,7 @@ __global__ __launch_bounds__(kProbeThreads) void probe_read_kernel(const u32x4* 
   sink[(long long)blockIdx.x * kProbeThreads + threadIdx.x] = acc;
 }
 
-__global__ __launch_bounds__(kProbeThreads) void probe_mfma_kernel(int iters, float* __restrict__ out) {
+__global__ __launch_bounds__(kProbeThreads, 8) void probe_mfma_kernel(int iters, float* __restrict__ out) {
   const int lane = threadIdx.x & 63;
   f16x8p a, b;
 #pragma unroll
