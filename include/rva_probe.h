@@ -19,20 +19,24 @@ extern "C" {
 /*
  * rva_probe_copy -- copy `bytes` (a multiple of 16, > 0) from src to dst
  * (16-byte aligned, not overlapping) with `grid` workgroups of 256 threads,
- * four 16-byte loads in flight per thread before their stores.
+ * 16-byte non-temporal loads and stores over a grid-stride loop (4
+ * workgroups per compute unit measured best).
  */
 int rva_probe_copy(const void* src, void* dst, long long bytes, int grid, void* stream);
 
 /*
  * rva_probe_read -- read `bytes` (a multiple of 16, > 0) of src (16-byte
- * aligned) with `grid` workgroups of 256 threads; each thread folds what it
- * read into one word written to sink (uint32, grid * 256 entries).
+ * aligned) with `grid` workgroups of 256 threads, four 16-byte
+ * non-temporal loads in flight per thread (2 workgroups per compute unit
+ * measured best); each thread folds what it read into one word written to
+ * sink (uint32, grid * 256 entries).
  */
 int rva_probe_read(const void* src, uint32_t* sink, long long bytes, int grid, void* stream);
 
 /*
  * rva_probe_mfma -- `iters` rounds of 8 independent 16x16x32 fp16 matrix-core
- * products per wave on register operands, `grid` workgroups of 4 waves;
+ * products per wave on register operands, `grid` workgroups of 4 waves
+ * (8 workgroups per compute unit, 8 waves per SIMD, measured best);
  * one float per thread to out (grid * 256 entries).  *flops (if not NULL)
  * receives the floating-point operations the launch performs.
  */
