@@ -84,8 +84,7 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // instructions: bit 1 is the non-temporal hint).  Q/K/V rows and output
 // rows are each touched once per launch.
 constexpr int kLoadAux = 0;   // Q loads and K/V staging loads
-constexpr int kStoreAux = 0;  // output rows
-constexpr bool kZeroNT = false;  // zero rows of pruned tokens as non-temporal stores
+constexpr int kStoreAux = 0;  // output rows and the zero rows of pruned tokens
 
 // Reductions over the four lanes l, l^16, l^32, l^48 that share a query:
 // a lane-swap exchanges 16-lane (resp. 32-lane) rows between two copies of
@@ -952,26 +951,24 @@ __device__ __forceinline__ void block32(Rsrc rq, Rsrc rk, Rsrc rv, Rsrc ro, int 
 
 // ---------------------------------------------------------------- kernels
 
-// Zero the output rows of pruned tokens of one (image, head); `o` points at
-// the head's slice of the image's first token row.  When `parts`
-// workgroups share the (image, head), this one takes its part `part` of
-// the 16-byte pieces.
+// Zero the output rows of the pruned tokens of one image for `nh`
+// consecutive heads: `ro` covers the image's rows from the first head's
+// slice of its first token row (rows `rs` bytes apart), `pruned` lists the
+// npruned pruned positions.  The heads' slices of a row are contiguous, so
+// a row is nh * 64 elements of 16-byte pieces, each thread keeping one
+// piece position and walking the rows.  When `parts` workgroups share the
+// image's heads, this one takes every parts-th row from row `part`.
 template <int NT, int ESIZE>
-__device__ __forceinline__ void zero_pruned(char* o, const uint64_t* ballots, int N, int H,
-                                            int part = 0, int parts = 1) {
-  constexpr int PIECES = kHeadDim * ESIZE / 16;
-  const uint32_t rs = (uint32_t)(H * kHeadDim * ESIZE);
-  const int total = N * PIECES;
-  for (int e = threadIdx.x + part * NT; e < total; e += parts * NT) {
-    const int j = e / PIECES, pc = e - j * PIECES;
-    const bool kept = (ballots[j >> 6] >> (j & 63)) & 1ull;
-    if (!kept) {
-      u32x4* dst = reinterpret_cast<u32x4*>(o + (uint32_t)j * rs + pc * 16);
-      if constexpr (kZeroNT)
-        __builtin_nontemporal_store(u32x4{0u, 0u, 0u, 0u}, dst);
-      else
-        *dst = u32x4{0u, 0u, 0u, 0u};
-    }
+__device__ __forceinline__ void zero_pruned(Rsrc ro, const uint16_t* pruned, int npruned, int nh,
+                                            uint32_t rs, int part = 0, int parts = 1) {
+  const int per = nh * (kHeadDim * ESIZE / 16);  // pieces per row, <= NT
+  const int rows = NT / per;                     // rows per sweep of the workgroup
+  const int j0 = (int)threadIdx.x / per;
+  const uint32_t pc = (uint32_t)((int)threadIdx.x - j0 * per) * 16u;
+  if (j0 >= rows) return;
+  for (int j = j0 + part * rows; j < npruned; j += parts * rows) {
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, ro, (int)(pruned[j] * rs + pc), 0,
+                                           kStoreAux);
   }
 }
 
@@ -1039,13 +1036,15 @@ __device__ __forceinline__ void attend_item(const AttnParams& p, int bid, unsign
   const uint32_t rs = (uint32_t)(H * kHeadDim);  // elements between consecutive token rows
   if constexpr (FUSED) {
     uint16_t* idx = reinterpret_cast<uint16_t*>(smem);
-    uint64_t* ballots = reinterpret_cast<uint64_t*>(smem + attn_ballots_off(N));
     int32_t* cnt = reinterpret_cast<int32_t*>(smem + attn_cnt_off(N));
-    const int n = compact_row<NT, uint16_t>(p.mask + (size_t)b * N, N, idx, nullptr, ballots, cnt);
+    const int n = compact_row<NT, uint16_t, true>(p.mask + (size_t)b * N, N, idx, nullptr, nullptr, cnt);
     unsigned char* kvbase = smem + attn_compact_bytes(N);
     const int h0 = hg * HG, h1 = min(H, h0 + HG);
     const uint32_t bytes = (uint32_t)N * rs * ES;
     auto roff = [=](int r) -> uint32_t { return (uint32_t)idx[min(r, n - 1)] * (rs * ES); };
+    // every head of the group at once: their slices of a row are contiguous
+    zero_pruned<NT, ES>(make_rsrc(rebase(p, ((size_t)b * N * H + h0) * kHeadDim, ES).o, bytes), idx + n,
+                        N - n, h1 - h0, rs * ES, t, S);
     if constexpr (DT != 0) {
       if (n > 0 && n <= p.rc) {
         // whole sequence resident: as many of the group's heads at once as
@@ -1055,8 +1054,6 @@ __device__ __forceinline__ void attend_item(const AttnParams& p, int bid, unsign
           const int nh = min(fit, h1 - h);
           if (h > h0) __syncthreads();  // the previous heads' staged rows are consumed
           const AttnParams pl = rebase(p, ((size_t)b * N * H + h) * kHeadDim, ES);
-          for (int j = 0; j < nh; ++j)
-            zero_pruned<NT, ES>(static_cast<char*>(pl.o) + j * kHeadDim * ES, ballots, N, H, t, S);
           if (t * kQBlock < n)  // the tile has query rows
             attend_resident16<DT, LANES_PER_TILE>(n, nh, p.scale_log2e, kvbase,
                                                   make_rsrc(pl.q, bytes), make_rsrc(pl.k, bytes),
@@ -1069,9 +1066,8 @@ __device__ __forceinline__ void attend_item(const AttnParams& p, int bid, unsign
     }
     for (int h = h0; h < h1; ++h) {
       if (h > hg * HG) __syncthreads();  // the previous head's staged rows are consumed
+      if (n <= 0) break;
       const AttnParams pl = rebase(p, ((size_t)b * N * H + h) * kHeadDim, ES);
-      zero_pruned<NT, ES>(static_cast<char*>(pl.o), ballots, N, H, t, S);
-      if (n <= 0) continue;
       if constexpr (DT == 0) {
         float* comb = reinterpret_cast<float*>(kvbase);
         for (int qb = t; qb * kQBlock < n; qb += S)

@@ -23,7 +23,10 @@ __device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
-__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+// The wave's index in its workgroup, through a first-lane read: the
+// compiler then knows it is the same in every lane, so arithmetic and
+// branches on it (unit and row assignments) run on the scalar unit.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 __device__ __forceinline__ int wave_max(int v) {
 #pragma unroll
@@ -203,11 +206,13 @@ __device__ __forceinline__ void mask_row_bytes(const uint8_t* __restrict__ mrow,
 // idx[0..n) in LDS and return n (the same value in every thread).  Each wave
 // takes 64-token chunks; a ballot gives every kept lane its rank inside the
 // chunk, a prefix over the (at most 16) chunk counts gives the chunk's base.
+// With PRUNED_TAIL the pruned positions follow in idx[n..N), ascending (a
+// pruned token j with r kept tokens before it goes to n + j - r).
 // Optionally stores rank[j] (-1 for a pruned token) and the per-chunk
 // ballots.  `cnt` holds one int per 64-token chunk.  Idx is int32_t or
 // uint16_t (positions are below 1024).  Contains two barriers; every
 // thread must call it.
-template <int NT, typename Idx = int32_t>
+template <int NT, typename Idx = int32_t, bool PRUNED_TAIL = false>
 __device__ int compact_bytes(const uint8_t (&mb)[compact_per<NT>()], int N, Idx* idx,
                              int32_t* rank, uint64_t* ballots, int32_t* cnt) {
   constexpr int W = NT / 64;
@@ -237,7 +242,10 @@ __device__ int compact_bytes(const uint8_t (&mb)[compact_per<NT>()], int N, Idx*
       for (int cc = 0; cc < c; ++cc) base += cnt[cc];
       const int j = c * 64 + lane;
       const int r = base + __popcll(bal[i] & lanemask_lt());
-      if (keep[i]) idx[r] = (Idx)j;
+      if (keep[i])
+        idx[r] = (Idx)j;
+      else if (PRUNED_TAIL && j < N)
+        idx[n + j - r] = (Idx)j;
       if (rank && j < N) rank[j] = keep[i] ? r : -1;
     }
   }
@@ -245,12 +253,12 @@ __device__ int compact_bytes(const uint8_t (&mb)[compact_per<NT>()], int N, Idx*
   return n;
 }
 
-template <int NT, typename Idx = int32_t>
+template <int NT, typename Idx = int32_t, bool PRUNED_TAIL = false>
 __device__ int compact_row(const uint8_t* __restrict__ mrow, int N, Idx* idx, int32_t* rank,
                            uint64_t* ballots, int32_t* cnt) {
   uint8_t mb[compact_per<NT>()];
   mask_row_bytes<NT>(mrow, N, mb);
-  return compact_bytes<NT, Idx>(mb, N, idx, rank, ballots, cnt);
+  return compact_bytes<NT, Idx, PRUNED_TAIL>(mb, N, idx, rank, ballots, cnt);
 }
 
 }  // namespace rva

@@ -93,11 +93,11 @@ struct LinearParams {
 __host__ __device__ inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
 
 
-// Compaction area at the start of the fused kernel's LDS: the kept list
-// uint16[N], then one ballot (u64) and one count (int32) per 64-token chunk.
+// Compaction area at the start of the fused kernel's LDS: the kept
+// positions then the pruned ones, uint16[N], then one count (int32) per
+// 64-token chunk.
 __host__ __device__ inline int attn_chunks(int N) { return (N + 63) >> 6; }
-__host__ __device__ inline size_t attn_ballots_off(int N) { return (size_t)round_up(N * 2, 16); }
-__host__ __device__ inline size_t attn_cnt_off(int N) { return attn_ballots_off(N) + (size_t)attn_chunks(N) * 8; }
+__host__ __device__ inline size_t attn_cnt_off(int N) { return (size_t)round_up(N * 2, 16); }
 __host__ __device__ inline size_t attn_compact_bytes(int N) {
   return (size_t)round_up((int)attn_cnt_off(N) + attn_chunks(N) * 4, 16);
 }
