@@ -506,13 +506,6 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// A workgroup barrier without the memory fence of __syncthreads (which would
-// also wait for the key chunk still in flight): this wave's LDS accesses
-// complete, then s_barrier.  The clobber keeps the compiler from moving
-// memory accesses across it.
-__device__ __forceinline__ void bar_lds() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
 
 // Streamed form (sequences longer than the whole-sequence staging): keys go
 // through two LDS buffers of kChunk16 rows, and the next chunk's loads are
@@ -601,7 +594,7 @@ __device__ __forceinline__ void attend_seq16(const AttnParams& p, int n, unsigne
       }
     }
     // the buffer of step s + 1 was read in step s - 1: every wave is past it
-    if (s > 0) bar_lds();
+    if (s > 0) lds_barrier();
     if (s + 1 < nsteps) {
       const int c1 = ((s + 1) % nchunk) * kChunk16;
       unsigned char* b = kvbase + ((s + 1) & 1) * 2 * kBuf;
@@ -612,7 +605,7 @@ __device__ __forceinline__ void attend_seq16(const AttnParams& p, int n, unsigne
       last_use();
       wait_vm<0>();  // nothing of this wave is left in flight into LDS
     }
-    bar_lds();  // every wave's loads of step s have landed
+    lds_barrier();  // every wave's loads of step s have landed
     const unsigned char* Ks = kvbase + (s & 1) * 2 * kBuf;
     const unsigned char* Vs = Ks + kBuf;
     const int rows = min(kChunk16, n - cc * kChunk16);
@@ -1149,14 +1142,6 @@ __global__ __launch_bounds__(kAttnThreads32) void attend32_kernel(AttnParams p) 
 // the item's first staging barrier, where its wave has already waited for
 // every earlier load, the atomic included.  The workgroup that leaves last
 // returns the counter to zero for the next launch.
-// A workgroup barrier that orders LDS only: this wave's LDS accesses
-// complete, then s_barrier; no wait for global memory, so the item boundary
-// does not wait for the item's output stores.  The clobber keeps the
-// compiler from moving memory accesses across it.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
 template <int DT>
 __global__ __launch_bounds__(kAttnThreads16, 3) void attend16_persistent_kernel(AttnParams p) {
   extern __shared__ __align__(16) unsigned char smem[];

@@ -28,6 +28,14 @@ __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 // branches on it (unit and row assignments) run on the scalar unit.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
+// A workgroup barrier that orders LDS only: this wave's LDS accesses
+// complete, then s_barrier.  Unlike __syncthreads it does not wait for the
+// wave's global loads and stores in flight.  The clobber keeps the compiler
+// from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 __device__ __forceinline__ int wave_max(int v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o));
@@ -210,8 +218,9 @@ __device__ __forceinline__ void mask_row_bytes(const uint8_t* __restrict__ mrow,
 // pruned token j with r kept tokens before it goes to n + j - r).
 // Optionally stores rank[j] (-1 for a pruned token) and the per-chunk
 // ballots.  `cnt` holds one int per 64-token chunk.  Idx is int32_t or
-// uint16_t (positions are below 1024).  Contains two barriers; every
-// thread must call it.
+// uint16_t (positions are below 1024).  Contains two LDS-only barriers
+// (loads and stores of the caller still in flight are not waited for);
+// every thread must call it.
 template <int NT, typename Idx = int32_t, bool PRUNED_TAIL = false>
 __device__ int compact_bytes(const uint8_t (&mb)[compact_per<NT>()], int N, Idx* idx,
                              int32_t* rank, uint64_t* ballots, int32_t* cnt) {
@@ -231,7 +240,7 @@ __device__ int compact_bytes(const uint8_t (&mb)[compact_per<NT>()], int N, Idx*
       if (ballots) ballots[c] = bal[i];
     }
   }
-  __syncthreads();
+  lds_barrier();
   int n = 0;
   for (int c = 0; c < nchunks; ++c) n += cnt[c];
 #pragma unroll
@@ -249,7 +258,7 @@ __device__ int compact_bytes(const uint8_t (&mb)[compact_per<NT>()], int N, Idx*
       if (rank && j < N) rank[j] = keep[i] ? r : -1;
     }
   }
-  __syncthreads();
+  lds_barrier();
   return n;
 }
 
