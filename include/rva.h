@@ -125,7 +125,9 @@ int rva_unpack(const void* o_packed, const int32_t* cu_seqlens, const uint8_t* m
  *                When either is given, one extra workgroup of the same launch
  *                computes them.
  *   max_seqlen_hint : as rva_ragged_attend's max_seqlen (<= 0 means N).
- * Results are identical to rva_pack + rva_ragged_attend + rva_unpack.
+ * Results are identical to rva_pack + rva_ragged_attend + rva_unpack when
+ * both launches take the same work decomposition (rva_set_query_split);
+ * otherwise they agree within the same error bounds.
  */
 int rva_fused(const void* q_pad, const void* k_pad, const void* v_pad, const uint8_t* mask,
               int B, int N, int H, int d, int max_seqlen_hint, float softmax_scale, int dtype,
@@ -135,9 +137,11 @@ int rva_fused(const void* q_pad, const void* k_pad, const void* v_pad, const uin
  * rva_fused_persistent -- rva_fused as a persistent grid: as many workgroups
  * as stay resident, each pulling rva_fused's work items (an image's head
  * pair, or one head of a tail image) from a device counter, one item ahead,
- * and running them with rva_fused's per-item code.  Same arguments and
- * results as rva_fused, bit for bit (16-bit inputs; fp32 falls back to
- * rva_fused), plus:
+ * and running them with rva_fused's per-item code.  Same arguments as
+ * rva_fused, and the same results bit for bit as rva_fused with one
+ * workgroup per (image, head) (16-bit inputs; fp32 falls back to rva_fused
+ * itself); small launches that rva_fused runs in the key-split form
+ * (rva_set_query_split) agree within the same error bounds.  Plus:
  *   work : int32[2] device scratch, all zero before the first call.  Every
  *          call leaves it zero again when it completes, so one buffer serves
  *          any number of stream-ordered calls.  Only one call may be in
@@ -363,12 +367,18 @@ int rva_layers_plan_create(const rva_layers_desc* desc, rva_plan* out);
  * default, 0, lets every launch choose from the device's compute units and
  * its length bound: fp32 takes one tile per 16-query block; 16-bit launches
  * with fewer (sequence, head) items than resident workgroup slots take as
- * many tiles as fill the slots (at most one 16-query block per wave), and
- * larger ones one workgroup per (sequence, head), or per head pair.
+ * many tiles as fill the slots (at most one 16-query block per wave) or,
+ * when one tile per 16-query block still fits one fill of the slots (and
+ * the sequences are staged whole), the key-split form: one block per
+ * workgroup, its key tiles split over the workgroup's waves and their
+ * partial results combined (the same attention in another order of
+ * summation); larger launches take one workgroup per (sequence, head), or
+ * per head pair.
  * split >= 1 forces that many tiles (at most one per 16-query block of the
  * length bound; 1 also turns head pairing off) on every later launch and
  * plan creation, except the persistent forms.  It exists for tests and
- * tuning: results stay within the same error bounds, identical bit for bit
+ * tuning (a forced split never takes the key-split form): results stay
+ * within the same error bounds, identical bit for bit across forced splits
  * for fp32 and for 16-bit sequences staged whole; a sequence streamed in key
  * chunks may differ in its last bits, because the chunk order of a query
  * block depends on which pass of its workgroup runs it.  RVA_ERR_INVALID

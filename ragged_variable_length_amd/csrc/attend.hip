@@ -811,6 +811,122 @@ __device__ __forceinline__ void attend_resident16(int n, int nh, float c, unsign
   }
 }
 
+// Key-split form of a whole sequence (launches whose one-block-per-workgroup
+// grid still fits one slot-fill, so that the workgroup's chain, not its
+// share of the device, sets the time): the workgroup stages the sequence's
+// K and V as the whole-sequence form does and takes the 16-query blocks qt,
+// qt + qs, ... (one, when the launch's length bound holds), and its four
+// waves split each block's 32-key tiles (wave w: tiles w, w + 4, ...)
+// instead of each walking every tile of blocks of its own.  Each wave keeps
+// a running max (rescaling at each of its tiles), its probability row sums
+// and a partial O; the partials are combined through LDS (`comb`,
+// kComb16Bytes).  A wave may have no tile: it then holds m = -inf, l = 0 and
+// O = 0, and weighs nothing in the combine.
+template <int DT, typename RowOff, typename Hook>
+__device__ __forceinline__ void attend_block_split16(int n, float c, unsigned char* kvbase, Rsrc rq,
+                                                     Rsrc rk, Rsrc rv, Rsrc ro, RowOff roff,
+                                                     Hook last_use, int qt, int qs,
+                                                     unsigned char* comb) {
+  typedef Half16<DT> Tr;
+  typedef typename Tr::T T;
+  typedef typename Tr::V4 V4;
+  typedef typename Tr::V8 V8;
+  constexpr int kWaves = kAttnThreads16 / 64;
+  constexpr uint32_t kHeadBytes = kHeadDim * 2;
+  const int lane = lane_id(), w = wave_id(), g = lane >> 4, r16 = lane & 15;
+  const int rows = round_up(n, kQBlock);
+  const int nqb = rows / kQBlock;
+  auto load_q = [&](int qb, V8 (&qf)[2]) {
+    const int q = qb * kQBlock + r16;
+    const uint32_t off = q < n ? roff(q) : kOOB;
+    qf[0] = __builtin_bit_cast(V8, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)(off + 16 * g), 0, kLoadAux));
+    qf[1] = __builtin_bit_cast(V8, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)(off + 64 + 16 * g), 0, kLoadAux));
+  };
+  V8 qf[2];
+  load_q(qt, qf);
+  unsigned char* Ks = kvbase;
+  unsigned char* Vs = kvbase + rows * kHeadBytes;
+  stage16<DT, kResidentMax16>(rk, rv, Ks, Vs, 0, n, kQBlock, roff);
+  __syncthreads();
+  last_use();
+  const int ntile = (n + kKeyTile - 1) / kKeyTile;
+  const FragLanes16 lanes = frag_lanes16();
+  // the output thread's row within a block (16 threads per row)
+  const int qq = (int)threadIdx.x >> 4, d0 = 4 * ((int)threadIdx.x & 15);
+  float* cm = reinterpret_cast<float*>(comb);  // [W][16] maxima
+  float* cl = cm + kWaves * 16;                 // [W][16] row sums
+  float* co = cl + kWaves * 16;                 // [W][16][kCombPitch32] partial O
+  for (int qb = qt; qb < nqb; qb += qs) {
+    if (qb > qt) {
+      load_q(qb, qf);
+      __syncthreads();  // the previous block's combine has read the partials
+    }
+    V8 ones;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ones[e] = (T)1.0f;
+    f32x4 o[5];
+#pragma unroll
+    for (int db = 0; db < 5; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m = -INFINITY;
+    for (int t = w; t < ntile; t += kWaves) {
+      const int k0 = t * kKeyTile;
+      V8 kf[2][2], vf[4];
+      k_frag16<DT>(Ks, k0, lanes, kf);
+      v_frag16<DT>(Vs, k0, lanes, k0 + kQBlock < rows, vf);
+      f32x4 s0, s1;
+      scores16<DT>(kf, qf, s0, s1);
+      mask_keys(s0, s1, n - k0);
+      // the tile's first key is valid, so its row max, and m, are finite
+      const float mn = fmaxf(m, quad_max(max8(s0, s1)) * c);
+      const float alpha = fast_exp2(m - mn);  // 0 at the wave's first tile
+      m = mn;
+#pragma unroll
+      for (int db = 0; db < 5; ++db) o[db] *= alpha;
+      V8 pf;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pf[e] = (T)fast_exp2(fmaf(s0[e], c, -m));
+        pf[4 + e] = (T)fast_exp2(fmaf(s1[e], c, -m));
+      }
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[db] = Tr::mfma(vf[db], pf, o[db]);
+      o[4] = Tr::mfma(ones, pf, o[4]);
+    }
+    if (g == 0) {
+      cm[w * 16 + r16] = m;
+      cl[w * 16 + r16] = o[4][0];
+    }
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+      *reinterpret_cast<f32x4*>(co + (w * 16 + r16) * kCombPitch32 + 16 * db + 4 * g) = o[db];
+    __syncthreads();
+    const int orow = qb * kQBlock + qq;
+    if (orow < n) {
+      float M = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < kWaves; ++i) M = fmaxf(M, cm[i * 16 + qq]);
+      float den = 0.f;
+      f32x4 num = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < kWaves; ++i) {
+        const float mi = cm[i * 16 + qq];
+        const float a = mi == -INFINITY ? 0.f : fast_exp2(mi - M);
+        den = fmaf(a, cl[i * 16 + qq], den);
+        const f32x4 part = *reinterpret_cast<const f32x4*>(co + (i * 16 + qq) * kCombPitch32 + d0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) num[e] = fmaf(a, part[e], num[e]);
+      }
+      // hardware reciprocal (about 1 ulp): ample for 16-bit outputs
+      const float inv = __builtin_amdgcn_rcpf(den);
+      V4 out;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) out[e] = (T)(num[e] * inv);
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, out), ro,
+                                            (int)(roff(orow) + 2 * d0), 0, kStoreAux);
+    }
+  }
+}
+
 // ---------------------------------------------------------------- fp32
 
 __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
@@ -989,7 +1105,10 @@ __device__ __forceinline__ AttnParams rebase(const AttnParams& p, size_t elem0, 
 // staging barrier, or after its zero fill when the image keeps no token
 // (the persistent form, which never splits, hands over its next item index
 // there).
-template <int DT, bool FUSED, bool LANES_PER_TILE = false, typename Hook>
+// KEYSPLIT: the launch takes the key-split form for sequences staged whole
+// (a kernel instance of its own, so that the other instances' registers are
+// not shaped by its code).
+template <int DT, bool FUSED, bool LANES_PER_TILE = false, bool KEYSPLIT = false, typename Hook>
 __device__ __forceinline__ void attend_item(const AttnParams& p, int bid, unsigned char* smem,
                                             Hook hook) {
   constexpr int NT = DT == 0 ? kAttnThreads32 : kAttnThreads16;
@@ -1047,11 +1166,18 @@ __device__ __forceinline__ void attend_item(const AttnParams& p, int bid, unsign
           const int nh = min(fit, h1 - h);
           if (h > h0) __syncthreads();  // the previous heads' staged rows are consumed
           const AttnParams pl = rebase(p, ((size_t)b * N * H + h) * kHeadDim, ES);
-          if (t * kQBlock < n)  // the tile has query rows
+          if (t * kQBlock >= n) {  // the tile has no query rows
+          } else if constexpr (KEYSPLIT) {
+            attend_block_split16<DT>(n, p.scale_log2e, kvbase, make_rsrc(pl.q, bytes),
+                                     make_rsrc(pl.k, bytes), make_rsrc(pl.v, bytes),
+                                     make_rsrc(pl.o, bytes), roff, hook, t, S,
+                                     kvbase + p.rc * (kHeadDim * 2 * 2) + kItemSlotBytes);
+          } else {
             attend_resident16<DT, LANES_PER_TILE>(n, nh, p.scale_log2e, kvbase,
                                                   make_rsrc(pl.q, bytes), make_rsrc(pl.k, bytes),
                                                   make_rsrc(pl.v, bytes), make_rsrc(pl.o, bytes),
                                                   roff, hook, t, S);
+          }
           h += nh;
         }
         return;
@@ -1089,10 +1215,17 @@ __device__ __forceinline__ void attend_item(const AttnParams& p, int bid, unsign
                 make_rsrc(pl.o, bytes), n, qb, p.scale_log2e, roff, comb);
     } else {
       if (n <= p.rc) {
-        if (t * kQBlock < n)
+        if (t * kQBlock >= n) {
+        } else if constexpr (KEYSPLIT) {
+          attend_block_split16<DT>(n, p.scale_log2e, smem, make_rsrc(pl.q, bytes),
+                                   make_rsrc(pl.k, bytes), make_rsrc(pl.v, bytes),
+                                   make_rsrc(pl.o, bytes), roff, hook, t, S,
+                                   smem + p.rc * (kHeadDim * 2 * 2));
+        } else {
           attend_resident16<DT>(n, 1, p.scale_log2e, smem, make_rsrc(pl.q, bytes),
                                 make_rsrc(pl.k, bytes), make_rsrc(pl.v, bytes),
                                 make_rsrc(pl.o, bytes), roff, hook, t, S);
+        }
       } else {
         attend_seq16<DT>(pl, n, smem, make_rsrc(pl.q, bytes), make_rsrc(pl.k, bytes),
                          make_rsrc(pl.v, bytes), make_rsrc(pl.o, bytes), roff, hook, t, S);
@@ -1101,7 +1234,7 @@ __device__ __forceinline__ void attend_item(const AttnParams& p, int bid, unsign
   }
 }
 
-template <int DT, bool FUSED>
+template <int DT, bool FUSED, bool KEYSPLIT = false>
 __device__ __forceinline__ void attend_body(const AttnParams& p, unsigned char* smem) {
   constexpr int NT = DT == 0 ? kAttnThreads32 : kAttnThreads16;
   int bid = blockIdx.x;
@@ -1114,14 +1247,14 @@ __device__ __forceinline__ void attend_body(const AttnParams& p, unsigned char* 
       --bid;
     }
   }
-  attend_item<DT, FUSED>(p, bid, smem, [] {});
+  attend_item<DT, FUSED, false, KEYSPLIT>(p, bid, smem, [] {});
 }
 
 // 16-bit: 4 waves, register budget for 3 waves per SIMD (3 workgroups per CU).
-template <int DT, bool FUSED>
+template <int DT, bool FUSED, bool KEYSPLIT = false>
 __global__ __launch_bounds__(kAttnThreads16, 3) void attend16_kernel(AttnParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
-  attend_body<DT, FUSED>(p, smem);
+  attend_body<DT, FUSED, KEYSPLIT>(p, smem);
 }
 
 template <bool FUSED>
@@ -1236,14 +1369,18 @@ static hipError_t set_lds_limit(const void* fn) {
 }
 
 hipError_t attend_init() {
-  const void* fns[8] = {reinterpret_cast<const void*>(&attend16_persistent_kernel<1>),
+  const void* fns[12] = {reinterpret_cast<const void*>(&attend16_persistent_kernel<1>),
                         reinterpret_cast<const void*>(&attend16_persistent_kernel<2>),
                         reinterpret_cast<const void*>(&attend32_kernel<false>),
                         reinterpret_cast<const void*>(&attend32_kernel<true>),
                         reinterpret_cast<const void*>(&attend16_kernel<1, false>),
                         reinterpret_cast<const void*>(&attend16_kernel<1, true>),
                         reinterpret_cast<const void*>(&attend16_kernel<2, false>),
-                        reinterpret_cast<const void*>(&attend16_kernel<2, true>)};
+                        reinterpret_cast<const void*>(&attend16_kernel<2, true>),
+                        reinterpret_cast<const void*>(&attend16_kernel<1, false, true>),
+                        reinterpret_cast<const void*>(&attend16_kernel<1, true, true>),
+                        reinterpret_cast<const void*>(&attend16_kernel<2, false, true>),
+                        reinterpret_cast<const void*>(&attend16_kernel<2, true, true>)};
   for (const void* f : fns) {
     hipError_t e = set_lds_limit(f);
     if (e != hipSuccess) return e;
@@ -1255,13 +1392,22 @@ hipError_t launch_attend(const AttnParams& p0, int dtype, bool fused, hipStream_
   AttnParams p = p0;
   const bool fused16 = fused && dtype != 0;
   p.rc = resident_rows(dtype, fused, p.N, fused16 ? kItemSlotBytes : 0);
-  const size_t lds = fused16 ? fused16_lds(p.N, p.rc) : attn_lds_bytes(dtype, fused, p.N, p.rc);
+  const size_t lds = (fused16 ? fused16_lds(p.N, p.rc) : attn_lds_bytes(dtype, fused, p.N, p.rc)) +
+                     (dtype != 0 && p.keysplit ? kComb16Bytes : 0);
   const int grid = (int)attend_grid_items(p, dtype, fused) +
                    ((fused && (p.cu_out || p.max_out)) ? 1 : 0);
   const dim3 blk(attn_threads(dtype));
   if (dtype == 0) {
     if (fused) hipLaunchKernelGGL((attend32_kernel<true>), dim3(grid), blk, lds, s, p);
     else hipLaunchKernelGGL((attend32_kernel<false>), dim3(grid), blk, lds, s, p);
+  } else if (p.keysplit) {
+    if (dtype == 1) {
+      if (fused) hipLaunchKernelGGL((attend16_kernel<1, true, true>), dim3(grid), blk, lds, s, p);
+      else hipLaunchKernelGGL((attend16_kernel<1, false, true>), dim3(grid), blk, lds, s, p);
+    } else {
+      if (fused) hipLaunchKernelGGL((attend16_kernel<2, true, true>), dim3(grid), blk, lds, s, p);
+      else hipLaunchKernelGGL((attend16_kernel<2, false, true>), dim3(grid), blk, lds, s, p);
+    }
   } else if (dtype == 1) {
     if (fused) hipLaunchKernelGGL((attend16_kernel<1, true>), dim3(grid), blk, lds, s, p);
     else hipLaunchKernelGGL((attend16_kernel<1, false>), dim3(grid), blk, lds, s, p);

@@ -399,6 +399,7 @@ int plan_grid(rva::AttnParams* p, int dtype, bool fused, bool persistent, long l
   p->heads_per_wg = 1;
   p->tail_b = 0;
   p->qsplit = 1;
+  p->keysplit = 0;
   int cus = 0;
   RVA_TRY(device_cus(&cus));
   const long long slots = 3LL * cus;
@@ -416,6 +417,12 @@ int plan_grid(rva::AttnParams* p, int dtype, bool fused, bool persistent, long l
   } else if (!persistent && bh < slots) {
     const int rc = rva::attend_resident_rows(dtype, fused, p->N);
     const bool whole = p->nbound <= rc;
+    if (whole && bh * nqb <= slots) {
+      // one query block per workgroup still fits one slot-fill: its four
+      // waves split the block's key tiles instead of walking them in turn
+      p->qsplit = nqb;
+      p->keysplit = 1;
+    } else {
     const long long per = whole ? (nqb + 3) / 4 : (nqb + 7) / 8;
     // streamed sequences: one pass over the keys per workgroup is worth up to
     // four slot-fills of workgroups (a second pass re-streams every key for
@@ -423,6 +430,7 @@ int plan_grid(rva::AttnParams* p, int dtype, bool fused, bool persistent, long l
     const long long fill = ((whole ? 1 : 4) * slots + bh - 1) / bh;
     const long long q = per < fill ? per : fill;
     p->qsplit = q > 1 ? (int)q : 1;
+    }
   }
   if (p->qsplit < 1) p->qsplit = 1;
   const long long n = rva::attend_grid_items(*p, dtype, fused);

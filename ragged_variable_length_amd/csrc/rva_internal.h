@@ -35,6 +35,10 @@ constexpr int kMaxSeq = 1024;  // longest sequence (= RVA_MAX_TOKENS)
 constexpr int kCombPitch32 = 68;
 constexpr int kComb32Bytes = (kAttnThreads32 / 64) * (16 + 16 + 16 * kCombPitch32) * 4;
 constexpr int kItemSlotBytes = 16;  // fused 16-bit LDS past the staging area (persistent item slot)
+// Key-split form (16-bit): LDS where the 4 waves' partial results of one
+// 16-query block are combined (per wave 16 maxima, 16 sums, 16 rows of 64
+// floats at a pitch of kCombPitch32), past the staging area.
+constexpr int kComb16Bytes = (kAttnThreads16 / 64) * (16 + 16 + 16 * kCombPitch32) * 4;
 
 struct AttnParams {
   const void* q;
@@ -54,6 +58,7 @@ struct AttnParams {
   int item_slot;          // persistent form: byte offset of its 4-byte item slot in dynamic LDS; set at launch
   int qsplit;             // query tiles per (sequence, head): one workgroup each (>= 1; 1 with head pairs)
   int nbound;             // host: longest sequence the launch is sized for (its length hint)
+  int keysplit;           // 16-bit whole sequences: 1 = one query block per workgroup, its key tiles split over the waves
 };
 
 struct CopyParams {

@@ -59,7 +59,14 @@ def test_persistent_equals_fused_and_oracle(device, name, make):
     work = torch.zeros(2, dtype=torch.int32, device=device)
     o1, cu1, mx1 = _outs(q, device)
     o2, cu2, mx2 = _outs(q, device)
-    rva.fused(q, k, v, mask, out=o1, cu_seqlens=cu1, max_seqlen=mx1, max_seqlen_hint=hint)
+    # the one-launch reference with one workgroup per (image, head): small
+    # launches would otherwise take the key-split form (another order of
+    # summation), which the persistent form does not have
+    rva.set_query_split(1)
+    try:
+        rva.fused(q, k, v, mask, out=o1, cu_seqlens=cu1, max_seqlen=mx1, max_seqlen_hint=hint)
+    finally:
+        rva.set_query_split(0)
     for _ in range(2):  # the second call checks the counter came back to zero
         o2.fill_(7.0)
         rva.fused_persistent(q, k, v, mask, work, out=o2, cu_seqlens=cu2, max_seqlen=mx2,
