@@ -84,7 +84,11 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // instructions: bit 1 is the non-temporal hint).  Q/K/V rows and output
 // rows are each touched once per launch.
 constexpr int kLoadAux = 0;   // Q loads and K/V staging loads
-constexpr int kStoreAux = 0;  // output rows and the zero rows of pruned tokens
+// Output rows (64 contiguous bytes of a row per store instruction) and the
+// zero rows of pruned tokens (whole rows), written once and never read back
+// by the launch: non-temporal.
+constexpr int kStoreAux = 2;
+constexpr int kZeroAux = 2;
 
 // Reductions over the four lanes l, l^16, l^32, l^48 that share a query:
 // a lane-swap exchanges 16-lane (resp. 32-lane) rows between two copies of
@@ -368,6 +372,11 @@ __device__ __forceinline__ void fixed_step16(const typename Half16<DT>::V8 (&vf)
 // Normalise one finished query block and store its rows: O^T block db,
 // lane (r16, g) holds O[q][16 db + 4 g .. + 3]; o[4] holds the query's
 // probability sum in every element.  Rows at kOOB are dropped.
+// Before the stores, one 16-lane row swap per pair of blocks (2 e, 2 e + 1)
+// trades lane-row parity g & 1 for the block parity: afterwards lane
+// (r16, g) holds O[q][32 e + 16 (g & 1) + 8 (g >> 1) .. + 7] in the pair,
+// so each store instruction writes 64 contiguous bytes of every row (two
+// per row in all) instead of 32.
 template <int DT>
 __device__ __forceinline__ void store_block16(const f32x4 (&o)[5], Rsrc ro, uint32_t qoff) {
   typedef Half16<DT> Tr;
@@ -376,13 +385,27 @@ __device__ __forceinline__ void store_block16(const f32x4 (&o)[5], Rsrc ro, uint
   const int g = lane_id() >> 4;
   // hardware reciprocal (about 1 ulp): ample for 16-bit outputs
   const float inv = __builtin_amdgcn_rcpf(o[4][0]);
+  u32x2 out[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) {
-    V4 out;
+    V4 x;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) out[j] = (T)(o[db][j] * inv);
-    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, out), ro,
-                                          (int)(qoff + db * 32 + 8 * g), 0, kStoreAux);
+    for (int j = 0; j < 4; ++j) x[j] = (T)(o[db][j] * inv);
+    out[db] = __builtin_bit_cast(u32x2, x);
+  }
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      // odd rows of the first operand trade places with even rows of the second
+      const auto sw = __builtin_amdgcn_permlane16_swap(out[2 * e][w], out[2 * e + 1][w], false, false);
+      out[2 * e][w] = sw[0];
+      out[2 * e + 1][w] = sw[1];
+    }
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4{out[2 * e][0], out[2 * e][1], out[2 * e + 1][0],
+                                                 out[2 * e + 1][1]},
+                                           ro, (int)(qoff + 64 * e + 32 * (g & 1) + 16 * (g >> 1)), 0,
+                                           kStoreAux);
   }
 }
 
@@ -1077,7 +1100,7 @@ __device__ __forceinline__ void zero_pruned(Rsrc ro, const uint16_t* pruned, int
   if (j0 >= rows) return;
   for (int j = j0 + part * rows; j < npruned; j += parts * rows) {
     __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, ro, (int)(pruned[j] * rs + pc), 0,
-                                           kStoreAux);
+                                           kZeroAux);
   }
 }
 
