@@ -1177,9 +1177,19 @@ __device__ __forceinline__ void attend_item(const AttnParams& p, int bid, unsign
     const int h0 = hg * HG, h1 = min(H, h0 + HG);
     const uint32_t bytes = (uint32_t)N * rs * ES;
     auto roff = [=](int r) -> uint32_t { return (uint32_t)idx[min(r, n - 1)] * (rs * ES); };
-    // every head of the group at once: their slices of a row are contiguous
-    zero_pruned<NT, ES>(make_rsrc(rebase(p, ((size_t)b * N * H + h0) * kHeadDim, ES).o, bytes), idx + n,
-                        N - n, h1 - h0, rs * ES, t, S);
+    auto zero_rows = [&] {
+      // every head of the group at once: their slices of a row are contiguous
+      zero_pruned<NT, ES>(make_rsrc(rebase(p, ((size_t)b * N * H + h0) * kHeadDim, ES).o, bytes),
+                          idx + n, N - n, h1 - h0, rs * ES, t, S);
+    };
+    // A whole sequence (16-bit, not key-split) issues its zero rows right
+    // after its staging barrier, so that they drain during the attention:
+    // issued before the staging loads, they would be part of the wait for
+    // them (the vector-memory counter counts stores too, in order).  A
+    // query tile without query rows stages nothing and writes its share at
+    // once.
+    const bool late_zero = DT != 0 && !KEYSPLIT && n > 0 && n <= p.rc && t * kQBlock < n;
+    if (!late_zero) zero_rows();
     if constexpr (DT != 0) {
       if (n > 0 && n <= p.rc) {
         // whole sequence resident: as many of the group's heads at once as
@@ -1199,7 +1209,12 @@ __device__ __forceinline__ void attend_item(const AttnParams& p, int bid, unsign
             attend_resident16<DT, LANES_PER_TILE>(n, nh, p.scale_log2e, kvbase,
                                                   make_rsrc(pl.q, bytes), make_rsrc(pl.k, bytes),
                                                   make_rsrc(pl.v, bytes), make_rsrc(pl.o, bytes),
-                                                  roff, hook, t, S);
+                                                  roff,
+                                                  [&] {
+                                                    if (h == h0) zero_rows();
+                                                    hook();
+                                                  },
+                                                  t, S);
           }
           h += nh;
         }
