@@ -425,6 +425,36 @@ def measure_ceilings(ctx):
             "vendor_fp16_matmul_8192_TFLOPs": round(2 * 8192 ** 3 / (mm_us * 1e-6) / 1e12, 1)}
 
 
+def measure_pattern(ctx, w):
+    """The headline's fused launch beside the library's gather probe
+    (csrc/probe.hip) on the same batch: the same reads and writes with none
+    of the arithmetic (non-temporal loads and stores, the fastest policy for
+    this pattern measured), both graph-timed warm and interleaved twice
+    (best of each).  probe / fused says how much of the
+    kernel's time its access pattern alone takes on this device."""
+    t, rva = ctx.torch, ctx.rva
+    tensors = upload(ctx, w)
+    q, k, v, mask = tensors
+    idx = rva.index(mask)
+    fused = fused_call(ctx, tensors, int(w.counts.max()))
+    out = t.empty_like(q)
+    probe = lambda: rva.probe_gather(q, k, v, mask, idx["cu_seqlens"], idx["kept_index"], out)
+    f_us, p_us = [], []
+    for _ in range(2):
+        f_us.append(ctx.graph_time(fused))
+        p_us.append(ctx.graph_time(probe))
+    f, p = min(f_us), min(p_us)
+    nbytes = workload_stats(w)["bytes_fused"]
+    del tensors, out, idx
+    return {"workload": w.name, "fused_us_warm": round(f, 2), "probe_us_warm": round(p, 2),
+            "fused_GBps": round(nbytes / (f * 1e-6) / 1e9, 1),
+            "probe_GBps": round(nbytes / (p * 1e-6) / 1e9, 1),
+            "probe_over_fused": round(p / f, 4),
+            "bytes": "the fused kernel's algorithmic bytes for both",
+            "kernel": "probe_gather_kernel: one workgroup per (image, head pair), kept rows' q/k/v "
+                      "slices read and every o row written, non-temporal loads and stores"}
+
+
 def measure_floor_cpp():
     """The C++ probe's dispatch floor (csrc/floor_bench.cpp, built next to the
     library), run as a child process; None when it has not been built."""
@@ -913,6 +943,8 @@ def main():
         floor["cpp"] = floor_cpp
         line["launch_floor"] = floor
         line["ceilings"] = measure_ceilings(ctx)
+        log("measuring the access pattern alone ...")
+        line["ceilings"]["access_pattern"] = measure_pattern(ctx, w)
         torch.cuda.empty_cache()
         per = []
         for wk in W.all_configs():

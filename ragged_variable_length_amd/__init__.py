@@ -95,6 +95,7 @@ def lib() -> ctypes.CDLL:
     L.rva_probe_copy.argtypes = [P, P, LL, I, P]
     L.rva_probe_read.argtypes = [P, P, LL, I, P]
     L.rva_probe_mfma.argtypes = [I, P, I, P, ctypes.POINTER(LL)]
+    L.rva_probe_gather.argtypes = [P, P, P, P, P, P, P, I, I, I, P]
     L.rva_threshold_l2_mask.argtypes = [P, I, I, I, I, ctypes.c_double, P, P]
     L.rva_qkv_projection.argtypes = [P, P, P, I, I, I, P, P, I, P, P, P, P]
     L.rva_out_projection.argtypes = [P, P, P, P, I, I, I, P, P, P, I, P, P]
@@ -108,7 +109,7 @@ def lib() -> ctypes.CDLL:
                  "rva_threshold_l2_mask", "rva_qkv_projection", "rva_out_projection",
                  "rva_layers_plan_create", "rva_fused_persistent",
                  "rva_fused_persistent_noalloc", "rva_set_query_split", "rva_probe_copy",
-                 "rva_probe_read", "rva_probe_mfma"):
+                 "rva_probe_read", "rva_probe_mfma", "rva_probe_gather"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -561,6 +562,21 @@ def probe_mfma(iters: int, out, grid: int, stream=None) -> int:
     _check(lib().rva_probe_mfma(int(iters), _ptr(out), int(grid), _stream(stream),
                                 ctypes.byref(fl)), "rva_probe_mfma")
     return fl.value
+
+
+def probe_gather(q, k, v, mask, cu_seqlens, kept_index, out, stream=None):
+    """Ceiling probe: rva_fused's reads and writes without its arithmetic.
+    q, k, v, out: padded 16-bit [B, N, H, 64]; mask uint8 [B, N];
+    cu_seqlens and kept_index as pack/index return them for that mask."""
+    (B, N, H, _), _ = _qkv(q, k, v)
+    if q.dtype == torch.float32:
+        raise ValueError("the gather probe takes 16-bit tensors")
+    m = _mask_u8(mask, B, N)
+    _dev(cu_seqlens, "cu_seqlens", dtype=torch.int32, shape=(B + 1,))
+    _dev(kept_index, "kept_index", dtype=torch.int32, numel=B * N)
+    _dev(out, "out", dtype=q.dtype, shape=tuple(q.shape))
+    _check(lib().rva_probe_gather(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(m), _ptr(cu_seqlens),
+                                  _ptr(kept_index), B, N, H, _stream(stream)), "rva_probe_gather")
 
 
 def empty(count: int = 1, stream=None):

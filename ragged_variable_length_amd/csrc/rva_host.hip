@@ -732,6 +732,23 @@ int rva_probe_mfma(int iters, float* out, int grid, void* stream, long long* flo
   return RVA_OK;
 }
 
+int rva_probe_gather(const void* q, const void* k, const void* v, void* o, const uint8_t* mask,
+                     const int32_t* cu_seqlens, const int32_t* kept_index, int B, int N, int H,
+                     void* stream) {
+  RVA_TRY(check_shape(B, N, H, RVA_HEAD_DIM, RVA_F16));
+  RVA_TRY(check_data(q, "q", true));
+  RVA_TRY(check_data(k, "k", true));
+  RVA_TRY(check_data(v, "v", true));
+  RVA_TRY(check_data(o, "o", true));
+  if (!mask) return fail(RVA_ERR_INVALID, "mask is NULL");
+  RVA_TRY(check_i32(cu_seqlens, "cu_seqlens", true));
+  RVA_TRY(check_i32(kept_index, "kept_index", true));
+  hipError_t e = rva::launch_probe_gather(q, k, v, o, mask, cu_seqlens, kept_index, B, N, H,
+                                          static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "gather probe launch");
+  return RVA_OK;
+}
+
 int rva_empty(int count, void* stream) {
   if (count < 0) return fail(RVA_ERR_INVALID, "count must be >= 0");
   for (int i = 0; i < count; ++i) {

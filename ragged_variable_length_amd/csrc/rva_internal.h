@@ -145,6 +145,9 @@ hipError_t launch_probe_copy(const void* src, void* dst, long long pieces, int g
 hipError_t launch_probe_read(const void* src, uint32_t* sink, long long pieces, int grid,
                              hipStream_t s);
 hipError_t launch_probe_mfma(int iters, float* out, int grid, hipStream_t s);
+hipError_t launch_probe_gather(const void* q, const void* k, const void* v, void* o,
+                               const uint8_t* mask, const int32_t* cu, const int32_t* kidx, int B,
+                               int N, int H, hipStream_t s);
 long long probe_mfma_flops(int iters, int grid);
 
 }  // namespace rva

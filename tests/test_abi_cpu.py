@@ -213,3 +213,17 @@ def test_probe_validation(L):
     assert L.rva_probe_read(FAKE, FAKE, LL(0), 4, None) == -1
     assert L.rva_probe_read(FAKE, FAKE, LL(1024), 0, None) == -1
     assert L.rva_probe_mfma(0, FAKE, 4, None, None) == -1
+    # gather probe: shapes as rva_fused (16-bit), every pointer present and aligned
+    g = L.rva_probe_gather
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 197, 12, None) == -1
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 197, 0, None) == -1
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 1 << 20, 12, None) == -1
+    assert g(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 197, 12, None) == -1
+    assert b"q" in L.rva_last_error()
+    assert g(FAKE, FAKE, FAKE, MIS, FAKE, FAKE, FAKE, 4, 197, 12, None) == -1
+    assert b"aligned" in L.rva_last_error()
+    assert g(FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 4, 197, 12, None) == -1
+    assert b"mask" in L.rva_last_error()
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 4, 197, 12, None) == -1
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 4, 197, 12, None) == -1
+    assert b"kept_index" in L.rva_last_error()
