@@ -612,7 +612,7 @@ def profile_commands(name, form="fused"):
                 "SQ_ACTIVE_INST_VALU SQ_BUSY_CU_CYCLES SQ_INSTS_VALU SQ_INSTS_MFMA "
                 "SQ_INSTS_VALU_TRANS_F32 SQ_WAVE_CYCLES SQ_INSTS_LDS GRBM_GUI_ACTIVE --output-format csv "
                 f"-d {d}_util -o fused {tgt}",
-        "all": _ROCPROF + "rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/prof_all "
+        "all": _ROCPROF + "rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/prof_all_trace "
                "-o bench -- python3 $R/bench.py --no-cpu",
     }
 
@@ -623,7 +623,7 @@ CU_NUM, SIMD_NUM, XCD_NUM = 256, 1024, 8
 
 def profile_kernel(w):
     """Kernel-name fragment of a workload's fused launch."""
-    return {"f16": "attend16_kernel<1, true>", "bf16": "attend16_kernel<2, true>",
+    return {"f16": "attend16_kernel<1, true, false>", "bf16": "attend16_kernel<2, true, false>",
             "f32": "attend32_kernel<true>"}[w.dtype]
 
 
