@@ -490,16 +490,21 @@ CPU_POOL_MAX = 16  # worker processes at most (the GPU machine's CPU share for one G
 
 def _oracle_images(args):
     """Pool worker: the oracle's pack + attend + unpack on images [b0, b1) of
-    the workload held by the parent (inherited through fork)."""
+    workload `name`, held by the parent (inherited through fork)."""
     import oracle
-    b0, b1 = args
-    w = _CPU_W
+    name, b0, b1 = args
+    w = _CPU_W[name]
     t0 = time.perf_counter()
     oracle.pack_attend_unpack(w.q[b0:b1], w.k[b0:b1], w.v[b0:b1], w.mask[b0:b1], w.dtype)
     return time.perf_counter() - t0
 
 
-_CPU_W = None
+_CPU_W = {}
+
+
+def _image_ranges(B, parts):
+    edges = [round(i * B / parts) for i in range(parts + 1)]
+    return [(edges[i], edges[i + 1]) for i in range(parts) if edges[i + 1] > edges[i]]
 
 
 def cpu_baseline_child(repeats=2):
@@ -508,12 +513,13 @@ def cpu_baseline_child(repeats=2):
     mixed batch, (i) in this one thread and (ii) over a pool of forked
     processes, one contiguous range of images each, one per available core
     (at most CPU_POOL_MAX).  Prints one JSON line."""
-    global _CPU_W
     import multiprocessing as mp
     import oracle
     import workloads as W
-    w = W.mixed_peak()
-    _CPU_W = w
+    configs = list(W.all_configs())
+    for wk in configs:
+        _CPU_W[wk.name] = wk
+    w = next(wk for wk in configs if wk.B == 1024)  # the headline's mixed batch
     model = ""
     try:
         for line in open("/proc/cpuinfo"):
@@ -528,15 +534,35 @@ def cpu_baseline_child(repeats=2):
         oracle.pack_attend_unpack(w.q, w.k, w.v, w.mask, w.dtype)
         one.append(time.perf_counter() - t0)
     cores = max(1, min(CPU_POOL_MAX, len(os.sched_getaffinity(0))))
-    edges = [round(i * w.B / cores) for i in range(cores + 1)]
-    parts = [(edges[i], edges[i + 1]) for i in range(cores) if edges[i + 1] > edges[i]]
     pool_s = []
+    per = []
     with mp.get_context("fork").Pool(cores) as pool:
-        pool.map(_oracle_images, [(0, 1)] * cores)  # workers up before timing
+        pool.map(_oracle_images, [(w.name, 0, 1)] * cores)  # workers up before timing
         for _ in range(repeats):
             t0 = time.perf_counter()
-            pool.map(_oracle_images, parts, chunksize=1)
+            pool.map(_oracle_images, [(w.name, b0, b1) for b0, b1 in _image_ranges(w.B, cores)],
+                     chunksize=1)
             pool_s.append(time.perf_counter() - t0)
+        # every configuration, the same two ways (best of `repeats` each)
+        for wk in configs:
+            t1 = []
+            for _ in range(repeats):
+                t0 = time.perf_counter()
+                oracle.pack_attend_unpack(wk.q, wk.k, wk.v, wk.mask, wk.dtype)
+                t1.append(time.perf_counter() - t0)
+            rng = _image_ranges(wk.B, cores)
+            tp = []
+            for _ in range(repeats):
+                t0 = time.perf_counter()
+                pool.map(_oracle_images, [(wk.name, b0, b1) for b0, b1 in rng], chunksize=1)
+                tp.append(time.perf_counter() - t0)
+            st = workload_stats(wk)
+            per.append({"workload": wk.name, "T": wk.total_kept,
+                        "single_thread_s": round(min(t1), 5),
+                        "single_thread_kept_tokens_per_s": round(wk.total_kept / min(t1), 1),
+                        "single_thread_gflops_fp64": round(st["flops"] / min(t1) / 1e9, 2),
+                        "pool_processes": len(rng), "pool_s": round(min(tp), 5),
+                        "pool_kept_tokens_per_s": round(wk.total_kept / min(tp), 1)})
     s1, sp = min(one), min(pool_s)
     print(json.dumps({
         "value": round(w.total_kept / sp, 1), "unit": "kept tokens/s", "cores": cores,
@@ -547,7 +573,7 @@ def cpu_baseline_child(repeats=2):
         "single_thread": {"value": round(w.total_kept / s1, 1), "cores": 1, "seconds": round(s1, 3),
                           "gflops_fp64": round(workload_stats(w)["flops"] / s1 / 1e9, 2)},
         "all_cores_gflops_fp64": round(workload_stats(w)["flops"] / sp / 1e9, 2),
-        "cpu_model": model}), flush=True)
+        "cpu_model": model, "per_config": per}), flush=True)
 
 
 def cpu_baseline():
