@@ -480,9 +480,24 @@ def measure_floor(ctx, reps):
     d_dev = ctx.events_time(lambda: rva.empty(1), reps)
     d_graph = ctx.graph_time(lambda: rva.empty(1))
     plan.close()
+    # the staged path's shape: four launches per call, direct and as one captured graph
+    t = ctx.torch
+    d4_lat = ctx.latency(lambda: rva.empty(4), reps)
+    rva.empty(4)
+    t.cuda.synchronize()
+    g4 = t.cuda.CUDAGraph()
+    with t.cuda.graph(g4):
+        rva.empty(4)
+    for _ in range(10):
+        g4.replay()
+    g4_lat = ctx.latency(g4.replay, reps)
+    del g4
     return {"graph_latency_us": round(g_lat, 2), "graph_back_to_back_us": round(g_dev, 2),
             "direct_latency_us": round(d_lat, 2), "direct_back_to_back_us": round(d_dev, 2),
-            "empty_kernel_device_us": round(d_graph, 2)}
+            "empty_kernel_device_us": round(d_graph, 2),
+            "direct_4_kernels_latency_us": round(d4_lat, 2),
+            "graph_4_kernels_latency_us": round(g4_lat, 2),
+            "note": "the persistent form is one direct launch: its floor is direct_latency_us"}
 
 
 CPU_POOL_MAX = 16  # worker processes at most (the GPU machine's CPU share for one GPU)
