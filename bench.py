@@ -455,14 +455,40 @@ def measure_pattern(ctx, w):
                       "slices read and every o row written, non-temporal loads and stores"}
 
 
+def _write_workload(path, w):
+    """A workload file for csrc/floor_bench.cpp: int32 B, N, H, dtype code,
+    length hint; q, k, v bits; the uint8 mask."""
+    import numpy as np
+    code = {"f32": 0, "f16": 1, "bf16": 2}[w.dtype]
+    with open(path, "wb") as f:
+        np.array([w.B, w.N, w.H, code, int(w.counts.max())], dtype=np.int32).tofile(f)
+        for a in (w.q, w.k, w.v):
+            np.ascontiguousarray(a).tofile(f)
+        np.ascontiguousarray(w.mask, dtype=np.uint8).tofile(f)
+
+
 def measure_floor_cpp():
     """The C++ probe's dispatch floor (csrc/floor_bench.cpp, built next to the
-    library), run as a child process; None when it has not been built."""
+    library), run as a child process; None when it has not been built.
+    Beside the empty kernel it times the fused call itself from C++ on the
+    small workloads (tiny, DeiT-S, DeiT-B 224 at 80% pruning), whose calls
+    the dispatch floor dominates."""
+    import shutil
     import subprocess
+    import tempfile
+    import workloads as W
     exe = os.path.join(ROOT, "ragged_variable_length_amd", "floor_bench")
     if not os.path.exists(exe):
         return None
-    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    tmp = tempfile.mkdtemp(prefix="rva_floor_")
+    try:
+        files = []
+        for w in (W.tiny(), W.deit_s_224_threshold_l2(), W.deit_b_224(0.8)):
+            files.append(os.path.join(tmp, w.name))
+            _write_workload(files[-1], w)
+        r = subprocess.run([exe] + files, capture_output=True, text=True, timeout=180)
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
     if r.returncode != 0:
         log("floor_bench failed:", r.stderr.strip())
         return None
