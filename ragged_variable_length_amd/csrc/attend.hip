@@ -35,9 +35,18 @@
 //    more than 2^8.  Either reference cancels exactly in the final division;
 //  * the fused form first compacts the image's keep-mask row in LDS, reads
 //    Q/K/V rows straight from the padded tensors through that list, writes
-//    O rows straight to padded positions and zero-fills pruned rows.  An
-//    optional extra workgroup computes cu_seqlens / max_seqlen in the same
-//    launch;
+//    O rows straight to padded positions and zero-fills pruned rows (for a
+//    sequence staged whole, right after its staging barrier, so that those
+//    stores drain during the attention rather than lengthen the wait for
+//    the staging loads).  An optional extra workgroup computes cu_seqlens /
+//    max_seqlen in the same launch;
+//  * O rows leave 64 contiguous bytes per row and store instruction (one
+//    16-lane row swap per pair of O blocks) and, like the zero rows, with
+//    the non-temporal hint: both are written once and never read back;
+//  * launches small enough that one workgroup per 16-query block fits one
+//    fill of the device take the key-split form: each workgroup one block,
+//    its four waves splitting the block's key tiles, partial results
+//    combined through LDS;
 //  * the persistent form runs the fused form's items (head pairs, tail
 //    heads) in a loop over a device work counter, one resident grid.
 // fp32 inputs use the 16x16x4 fp32 matrix-core product (no precision is
