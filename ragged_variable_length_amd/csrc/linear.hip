@@ -26,8 +26,10 @@
 // barrier per stage orders both.  16-byte pieces are XOR-swizzled by row so
 // that the 16-byte operand reads are conflict-free.  The 16x16x32
 // matrix-core product is taken transposed, D^T = W X^T, so that each lane
-// ends with four adjacent output columns of one row: one 8-byte store per
-// 16x16 block.  Tiles are dealt to the XCDs in round-robin groups of two row
+// ends with four adjacent output columns of one row; a 16-lane row swap per
+// pair of 16x16 blocks gives it eight, so the epilogue reads bias and
+// residual and writes output 16 bytes per lane (64 contiguous bytes of a row
+// per instruction), with non-temporal stores.  Tiles are dealt to the XCDs in round-robin groups of two row
 // blocks (all their column tiles), so a group's input rows are reused from
 // one XCD's L2 and the live row blocks (below the device-side row count)
 // spread over every XCD.
@@ -230,35 +232,64 @@ __device__ __forceinline__ void linear_tile(const LinearParams& p, int mb, int n
   wait_vm<0>();
 
   // epilogue: acc[i][j] lane (r16, g) holds out[m][n .. n+3] with
-  // m = m0 + kLinTM wm + 16 j + r16, n = n0 + kLinTN wn + 16 i + 4 g
-  const int ng = p.Nout / p.y_split;  // columns per output group
+  // m = m0 + kLinTM wm + 16 j + r16, n = n0 + kLinTN wn + 16 i + 4 g.  One
+  // 16-lane row swap per pair of column blocks (2e, 2e + 1) trades lane-row
+  // parity g & 1 for the block parity: lane (r16, g) then holds the eight
+  // columns 32 e + 16 (g & 1) + 8 (g >> 1) .. + 7 of its row (the first four
+  // in acc[2e][j], the next four in acc[2e + 1][j]), so bias, residual and
+  // output move 16 bytes per lane and 64 contiguous bytes of a row per
+  // instruction.  Every lane takes part in the swaps before any row check.
+  static_assert(NI % 2 == 0, "column blocks in pairs");
+#pragma unroll
+  for (int e = 0; e < NI / 2; ++e)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc[2 * e][j][t]),
+                                                         __float_as_uint(acc[2 * e + 1][j][t]), false,
+                                                         false);
+        acc[2 * e][j][t] = __uint_as_float(sw[0]);
+        acc[2 * e + 1][j][t] = __uint_as_float(sw[1]);
+      }
+  const int ng = p.Nout / p.y_split;  // columns per output group (a multiple of 64)
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int m = m0 + wm * kLinTM + 16 * j + r16;
     if (m >= M) continue;
     const int orow = p.y_index ? p.y_index[m] : m;
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int n = n0 + wn * kLinTN + 16 * i + 4 * g;
+    for (int e = 0; e < NI / 2; ++e) {
+      const int n = n0 + wn * kLinTN + 32 * e + 16 * (g & 1) + 8 * (g >> 1);
       if (n >= p.Nout) continue;
-      float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+      float v[8];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        v[t] = acc[2 * e][j][t];
+        v[4 + t] = acc[2 * e + 1][j][t];
+      }
       if (p.bias) {
-        const u32x2 bb = *reinterpret_cast<const u32x2*>(static_cast<const char*>(p.bias) + (size_t)n * 2);
-        v[0] += to_f32<DT>(bb[0] & 0xFFFFu);
-        v[1] += to_f32<DT>(bb[0] >> 16);
-        v[2] += to_f32<DT>(bb[1] & 0xFFFFu);
-        v[3] += to_f32<DT>(bb[1] >> 16);
+        const u32x4 bb = *reinterpret_cast<const u32x4*>(static_cast<const char*>(p.bias) + (size_t)n * 2);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          v[2 * t] += to_f32<DT>(bb[t] & 0xFFFFu);
+          v[2 * t + 1] += to_f32<DT>(bb[t] >> 16);
+        }
       }
       const int grp = n / ng, col = n - grp * ng;
       const size_t eoff = ((size_t)orow * ng + col) * 2;
       if (p.residual) {
-        const u32x2 rr = *reinterpret_cast<const u32x2*>(static_cast<const char*>(p.residual) + eoff);
-        v[0] += to_f32<DT>(rr[0] & 0xFFFFu);
-        v[1] += to_f32<DT>(rr[0] >> 16);
-        v[2] += to_f32<DT>(rr[1] & 0xFFFFu);
-        v[3] += to_f32<DT>(rr[1] >> 16);
+        const u32x4 rr = *reinterpret_cast<const u32x4*>(static_cast<const char*>(p.residual) + eoff);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          v[2 * t] += to_f32<DT>(rr[t] & 0xFFFFu);
+          v[2 * t + 1] += to_f32<DT>(rr[t] >> 16);
+        }
       }
-      *reinterpret_cast<u32x2*>(static_cast<char*>(p.y[grp]) + eoff) = pack4<DT>(v[0], v[1], v[2], v[3]);
+      const u32x2 lo = pack4<DT>(v[0], v[1], v[2], v[3]), hi = pack4<DT>(v[4], v[5], v[6], v[7]);
+      // written once, never read back by the launch: non-temporal
+      __builtin_nontemporal_store(u32x4{lo[0], lo[1], hi[0], hi[1]},
+                                  reinterpret_cast<u32x4*>(static_cast<char*>(p.y[grp]) + eoff));
     }
   }
 }
@@ -272,7 +303,8 @@ __device__ __forceinline__ void linear_zero_rows(const LinearParams& p, int z) {
   for (int e = threadIdx.x; e < rows * pieces; e += kLinThreads) {
     const int r = r0 + e / pieces, pc = e % pieces;
     if (!p.zero_mask[r])
-      *reinterpret_cast<u32x4*>(y + ((size_t)r * p.Nout) * 2 + (size_t)pc * 16) = u32x4{0u, 0u, 0u, 0u};
+      __builtin_nontemporal_store(u32x4{0u, 0u, 0u, 0u},
+                                  reinterpret_cast<u32x4*>(y + ((size_t)r * p.Nout) * 2 + (size_t)pc * 16));
   }
 }
 
