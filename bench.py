@@ -655,6 +655,10 @@ COPY_PROBE_KERNEL = "probe_copy_kernel"
 # DeiT-B configurations the pages' kernel-latency claim is about
 PROFILE_WORKLOADS = {
     "mixed_b1024": lambda W: W.mixed_peak(),
+    "tiny": lambda W: W.tiny(),
+    "deit_s_224": lambda W: W.deit_s_224_threshold_l2(),
+    "deit_b_224_p0": lambda W: W.deit_b_224(0.0),
+    "deit_b_224_p20": lambda W: W.deit_b_224(0.2),
     "deit_b_224_p50": lambda W: W.deit_b_224(0.5),
     "deit_b_224_p80": lambda W: W.deit_b_224(0.8),
     "deit_b_384_p80": lambda W: W.deit_b_384(),
@@ -688,9 +692,23 @@ PROFILE_COMMANDS = profile_commands("mixed_b1024")
 CU_NUM, SIMD_NUM, XCD_NUM = 256, 1024, 8
 
 
+def kernel_label(w):
+    """Name of the fused instance a workload's launch runs: the key-split
+    form when one workgroup per 16-query block of the longest sequence fits
+    one fill of 3 workgroups per CU (on 256 CUs) and that sequence is staged
+    whole (208 rows at N = 197)."""
+    if w.dtype == "f32":
+        return "attend32_kernel<true>"
+    nqb = -(-int(w.counts.max()) // 16)
+    ks = w.B * w.H * nqb <= 3 * 256 and w.B * w.H < 3 * 256 and int(w.counts.max()) <= 208
+    return f"{profile_kernel(w)}, {'true' if ks else 'false'}>"
+
+
 def profile_kernel(w):
-    """Kernel-name fragment of a workload's fused launch."""
-    return {"f16": "attend16_kernel<1, true, false>", "bf16": "attend16_kernel<2, true, false>",
+    """Kernel-name fragment of a workload's fused launch (the 16-bit fused
+    instances: whole-sequence and streamed forms, or the key-split form of
+    small launches)."""
+    return {"f16": "attend16_kernel<1, true", "bf16": "attend16_kernel<2, true",
             "f32": "attend32_kernel<true>"}[w.dtype]
 
 
@@ -1006,7 +1024,7 @@ def main():
                              "zero-filled padded output)"},
         "roofline": {"bound": rl["bound"], "achieved": rl["GBps"], "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": rl["frac_hbm"], "traffic": traffic,
-                     "kernel": f"{profile_kernel(w)} (fused, {w.dtype})",
+                     "kernel": f"{kernel_label(w)} (fused, {w.dtype})",
                      "algorithmic_bytes_per_launch": stats["bytes_fused"],
                      "avg_launch_us": round(dev_us, 3),
                      "mfma_TFLOPs": rl["TFLOPs"], "mfma_frac": rl["frac_mfma"]},
