@@ -134,7 +134,9 @@ int validate_pack(const void* q_pad, const void* k_pad, const void* v_pad, const
   p.N = N;
   p.row_bytes = (int)(H * d * esize(dtype));
   out->max_seqlen = max_seqlen;
-  out->splits = copy_splits(B, N);
+  // splits only help copies: an index-only pack (no rows) takes one
+  // workgroup per image, each compacting its mask row once
+  out->splits = (in[0] || in[1] || in[2]) ? copy_splits(B, N) : 1;
   return RVA_OK;
 }
 
