@@ -109,11 +109,14 @@ __host__ __device__ inline int linear_tile_slots(int m_tiles, int n_tiles) {
 
 typedef __attribute__((address_space(3))) void* LdsPtr;
 
-// Swizzle key of row r: piece p of the row is stored at slot p ^ key(r).  For
-// 64-element rows the key is r mod 8; for 32-element rows (four pieces, four
-// rows per 256 bytes of banks) it is (r / 4) mod 4, so the 16 rows of a
-// 16-lane operand read hit 16 distinct bank groups.
-__device__ __forceinline__ int lin_key(int r) { return kLinK == 64 ? (r & 7) : ((r >> 2) & 3); }
+// Swizzle key of row r: piece p of the row is stored at slot p ^ key(r).  A
+// 16-byte LDS read is served 8 lanes (128 bytes, every bank once) at a time,
+// and the 8 lanes of an operand read take the same piece of 8 consecutive
+// rows.  A 64-element row fills the 128 bytes of banks, so the key is r mod 8;
+// two 32-element rows share them (r and r + 1 in opposite halves), so the key
+// is (r / 2) mod 4.  (Hardware counters: no bank conflicts with either; the
+// key (r / 4) mod 4 cost four conflict cycles per 32-element read.)
+__device__ __forceinline__ int lin_key(int r) { return kLinK == 64 ? (r & 7) : ((r >> 1) & 3); }
 
 // byte offset of 16-byte piece p of row r in a staged [rows][kLinK] half tile
 __device__ __forceinline__ int lin_swz(int r, int p) { return r * kLinPitch + ((p ^ lin_key(r)) << 4); }
