@@ -685,6 +685,9 @@ def profile_commands(name, form="fused"):
                 f"-d {d}_util -o fused {tgt}",
         "all": _ROCPROF + "rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/prof_all_trace "
                "-o bench -- python3 $R/bench.py --no-cpu",
+        "short": _ROCPROF + "rocprofv3 --kernel-trace --stats --output-format csv -d "
+                 "$R/gpurun_out/prof_short_trace -o bench -- python3 $R/bench.py --gpus 1 --steps 20 "
+                 "--warmup 5 > $R/gpurun_out/prof_short_line.json",
     }
 
 
@@ -844,6 +847,46 @@ def summarize_all(trace_dir, cmds, top=30):
     print("\n".join(lines))
 
 
+def summarize_short(trace_dir, line_file, warmup=5, steps=20):
+    """The headline's own dispatches in a kernel trace of a short bench run
+    (`--steps 20 --warmup 5`): the first warmup + steps launches of the mixed batch's fused
+    kernel (6529 workgroups; the process's first GPU work), the last `steps`
+    of them timed, against the launch time the line reports from HIP events
+    in the same run."""
+    import glob
+    import workloads as W
+    w = W.mixed_peak()
+    kern = kernel_label(w)
+    rows = _read_csv(glob.glob(os.path.join(trace_dir, "*kernel_trace.csv"))[0])
+    mine = []
+    for r in rows:
+        wg = int(r["Workgroup_Size_X"]) * int(r["Workgroup_Size_Y"]) * int(r["Workgroup_Size_Z"])
+        grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"]) // max(wg, 1)
+        if kern in r["Kernel_Name"] and grid == 6529:
+            mine.append((int(r["Start_Timestamp"]), (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+    mine.sort()
+    durs = [d for _, d in mine[:warmup + steps]]
+    timed = durs[warmup:]
+    with open(line_file) as f:
+        line = json.loads([ln for ln in f.read().splitlines() if ln.startswith("{")][-1])
+    ev = line["roofline"]["avg_launch_us"]
+    lines = [f"# Fused kernel, {w.name}: the headline's dispatches in a short bench run (5 warm-ups, 20 timed launches)", "",
+             "Command (from the repository root, after building):", "",
+             "```", PROFILE_COMMANDS["short"], "```", "",
+             f"The headline's launches are the process's first GPU work: `{kern}` with 6529 workgroups, "
+             f"{warmup} warm-up and {steps} timed launches (later launches of the same shape belong to the "
+             "per-workload section and are not counted here).", "",
+             "| launch | us |", "|---|---|"]
+    lines += [f"| {'warm-up' if i < warmup else 'timed'} {i + 1} | {d:.2f} |" for i, d in enumerate(durs)]
+    lines += ["", "| | us |", "|---|---|",
+              f"| mean of the {len(timed)} timed dispatches (rocprofv3) | {statistics.mean(timed):.2f} |",
+              f"| the line's `roofline.avg_launch_us` (HIP events, same run) | {ev:.2f} |",
+              f"| ratio | {ev / statistics.mean(timed):.4f} |"]
+    with open(os.path.join(ROOT, "profiles", "fused_mixed_b1024_short_run_trace.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def summarize_util(util_dir, name="mixed_b1024", form="fused"):
     """Matrix-core and VALU utilisation of the fused kernel from the "util"
     counter run: MfmaUtil = MFMA busy cycles / (GUI-active cycles x SIMDs),
@@ -919,6 +962,8 @@ def main():
                     help="launch form of a --profile run, and of --summarize-util")
     ap.add_argument("--summarize-all", metavar="TRACE_DIR",
                     help="write the profiles/ summary of every kernel from a traced full bench run")
+    ap.add_argument("--summarize-short", nargs=2, metavar=("TRACE_DIR", "LINE_JSON"),
+                    help="summarise a kernel trace of a short run (PROFILE_COMMANDS['short'])")
     ap.add_argument("--summarize-util", metavar="UTIL_DIR",
                     help="write the profiles/ utilisation summary from the rocprofv3 counter run")
     ap.add_argument("--cpu-baseline-child", action="store_true", help=argparse.SUPPRESS)
@@ -928,6 +973,9 @@ def main():
         return
     if args.summarize_all:
         summarize_all(args.summarize_all, PROFILE_COMMANDS)
+        return
+    if args.summarize_short:
+        summarize_short(*args.summarize_short)
         return
     if args.summarize_util:
         summarize_util(args.summarize_util, args.name, args.form)
