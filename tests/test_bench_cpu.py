@@ -74,3 +74,37 @@ def test_image_ranges_cover_every_image_once(B, parts):
     covered = np.concatenate([np.arange(b0, b1) for b0, b1 in rng])
     assert np.array_equal(covered, np.arange(B))
     assert len(rng) == min(B, parts)
+
+
+def test_short_run_summary_takes_the_headlines_first_dispatches(tmp_path, monkeypatch):
+    """The short-run trace summary counts the first warm-up + timed
+    dispatches of the mixed batch's fused launch shape (later dispatches of
+    that shape and other kernels are not the headline's) and compares the
+    timed ones with the line's HIP-event figure."""
+    import csv
+    trace = tmp_path / "trace"
+    trace.mkdir()
+    (tmp_path / "profiles").mkdir()
+    kern = "void rva::" + bench.kernel_label(W.mixed_peak()) + "(rva::AttnParams)"
+    fields = ["Kernel_Name", "Start_Timestamp", "End_Timestamp", "Workgroup_Size_X", "Workgroup_Size_Y",
+              "Workgroup_Size_Z", "Grid_Size_X", "Grid_Size_Y", "Grid_Size_Z"]
+    rows, t = [], 10_000
+    for i in range(40):  # 25 headline dispatches, then 15 more of the same shape (1000 us each)
+        d = (100 + i) * 1000 if i < 25 else 1_000_000
+        rows.append([kern, t, t + d, 256, 1, 1, 6529 * 256, 1, 1])
+        rows.append(["void rva::other_kernel()", t + d, t + d + 5000, 256, 1, 1, 256, 1, 1])
+        t += d + 10_000
+    rows.append([kern, t, t + 7_000_000, 256, 1, 1, 100 * 256, 1, 1])  # another launch shape
+    with open(trace / "bench_kernel_trace.csv", "w", newline="") as f:
+        wr = csv.writer(f)
+        wr.writerow(fields)
+        wr.writerows(rows[::-1])  # order in the file does not matter
+    line = tmp_path / "line.json"
+    line.write_text("noise\n" + json.dumps({"roofline": {"avg_launch_us": 115.0}}) + "\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    bench.summarize_short(str(trace), str(line))
+    text = (tmp_path / "profiles" / "fused_mixed_b1024_short_run_trace.md").read_text()
+    want = sum(100 + i for i in range(5, 25)) / 20  # timed: dispatches 6..25
+    assert f"| mean of the 20 timed dispatches (rocprofv3) | {want:.2f} |" in text
+    assert "| warm-up 5 | 104.00 |" in text and "| timed 25 | 124.00 |" in text
+    assert f"| ratio | {115.0 / want:.4f} |" in text
