@@ -1072,7 +1072,8 @@ def main():
                      "algorithmic_bytes_per_launch": stats["bytes_fused"],
                      "avg_launch_us": round(dev_us, 3),
                      "mfma_TFLOPs": rl["TFLOPs"], "mfma_frac": rl["frac_mfma"]},
-        "warm_state": ("fresh process: the W warm-up launches are its first GPU work (the first ~100 "
+        "warm_state": ("after the calibration probes (profiling run)" if args.profile else
+                       "fresh process: the W warm-up launches are its first GPU work (the first ~100 "
                        "launches of a fresh process run up to 15% slower; per_config's entry for this "
                        "workload gives the warm kernel time)"),
     }
