@@ -1027,7 +1027,7 @@ def main():
         args.quick = args.no_cpu = True
 
     # The headline runs first: its W warm-up and K timed launches are the
-    # first GPU work of this process.  A fresh process's first ~100 launches
+    # first kernel launches of this process (after the input upload).  A fresh process's first ~100 launches
     # run up to 15% slower while the device's power management settles, so
     # with few warm-ups the line measures that state; the warm figures (the
     # per-workload section's, after its own warm-ups) sit beside it.
@@ -1073,7 +1073,7 @@ def main():
                      "avg_launch_us": round(dev_us, 3),
                      "mfma_TFLOPs": rl["TFLOPs"], "mfma_frac": rl["frac_mfma"]},
         "warm_state": ("after the calibration probes (profiling run)" if args.profile else
-                       "fresh process: the W warm-up launches are its first GPU work (the first ~100 "
+                       "fresh process: the W warm-up launches are its first kernel launches (the first ~100 "
                        "launches of a fresh process run up to 15% slower; per_config's entry for this "
                        "workload gives the warm kernel time)"),
     }
