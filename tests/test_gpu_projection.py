@@ -54,6 +54,7 @@ CASES = [
     (3, 5, 50, 64, "f16"),       # one head, K = 64 (single K stage)
     (4, 2, 577, 192, "bf16"),    # 384x384 token count, DeiT-T width
     (5, 7, 33, 320, "f16"),      # Nout = 960, C not a multiple of 128
+    (6, 2, 197, 1024, "bf16"),   # ViT-L width: 16 K stages, Nout = 3072 (12 column tiles)
 ]
 
 
