@@ -535,3 +535,34 @@ def test_split_setting_rejects_negative(device):
     rva = _rva()
     with pytest.raises(rva.RVAError):
         rva.set_query_split(-1)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_vit_l_mixed_batch(device, dtype):
+    """A ViT-L/14 shape (257 tokens, 16 heads) with per-image pruning rates
+    uniform in [0, 0.9], 256 images: head pairs, sequences staged whole and
+    (past the whole-sequence capacity) in chunks within one launch.  Fused
+    and packed forms against the oracle, every row."""
+    rva = _rva()
+    B, N, H = 256, 257, 16
+    rng = np.random.Generator(np.random.PCG64(71 if dtype == "f16" else 72))
+    p = rng.uniform(0.0, 0.9, size=B)
+    counts = np.clip(np.rint((1.0 - p) * N), 1, N).astype(int).tolist()
+    w = W.random_workload(73 if dtype == "f16" else 74, B=B, N=N, H=H, dtype=dtype, counts=counts,
+                          name=f"vit_l_{dtype}")
+    _say(f"[vit-l] {dtype} B={B} N={N} H={H}")
+    q, k, v, mask = upload(w, device)
+    o = torch.full_like(q, float("nan"))
+    pk = rva.pack(q, k, v, mask)
+    o2 = torch.full_like(pk["q"], float("nan"))
+    rva.fused(q, k, v, mask, out=o, max_seqlen_hint=max(counts))
+    rva.ragged_attend(pk["q"], pk["k"], pk["v"], pk["cu_seqlens"], max(counts), out=o2)
+    torch.cuda.synchronize()
+    ref, cu_ref, _, _ = oracle.pack_attend_unpack(w.q, w.k, w.v, w.mask, w.dtype)
+    err = max_err(f64(o), ref)
+    _say(f"   fused max abs err {err:.3e}")
+    assert err <= TOL[w.dtype]
+    assert (bits(o)[w.mask == 0] == 0).all()
+    T = int(cu_ref[-1])
+    ref_pk = ref.reshape(-1, H, w.d)[oracle.kept_index(w.mask)]
+    assert max_err(f64(o2[:T]), ref_pk) <= TOL[w.dtype]
